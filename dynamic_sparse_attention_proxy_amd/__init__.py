@@ -1,0 +1,219 @@
+"""CRISP sparse prefill on AMD MI355X: Python binding of ``libcrisp.so``.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C-ABI declared in ``include/crisp.h``.  PyTorch supplies device
+memory and the stream.  Importing works without a GPU; calling a compute
+entry point without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcrisp.so")
+
+F32, BF16 = 0, 1
+SELECT_NOISE_FLOOR, SELECT_KEEP_ALL = 0, 1
+
+STATUS = {0: "CRISP_OK", -1: "CRISP_ERR_NULL", -2: "CRISP_ERR_SHAPE", -3: "CRISP_ERR_DTYPE",
+          -4: "CRISP_ERR_CONFIG", -5: "CRISP_ERR_WORKSPACE", -6: "CRISP_ERR_CAPACITY", -7: "CRISP_ERR_HIP",
+          -8: "CRISP_ERR_ALIGN"}
+
+EXPORTS = ["crisp_workspace_size", "crisp_index_capacity", "crisp_route", "crisp_select_indices",
+           "crisp_sparse_prefill", "crisp_dense_prefill", "crisp_status_string"]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("w_sink", ctypes.c_int32), ("w_local", ctypes.c_int32),
+                ("tau_num", ctypes.c_uint32), ("tau_den", ctypes.c_uint32),
+                ("alpha_num", ctypes.c_uint32), ("alpha_den", ctypes.c_uint32),
+                ("gamma_num", ctypes.c_uint32), ("gamma_den", ctypes.c_uint32),
+                ("select_mode", ctypes.c_int32)]
+
+
+class RelBias(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("offsets", ctypes.c_void_p), ("values", ctypes.c_void_p)]
+
+
+class IndexSets(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_void_p), ("cstruct_num", ctypes.c_void_p), ("mass_v", ctypes.c_void_p),
+                ("mass_s", ctypes.c_void_p), ("mass_total", ctypes.c_void_p), ("vs_count", ctypes.c_void_p),
+                ("vs_vertical", ctypes.c_void_p), ("vs_slash", ctypes.c_void_p),
+                ("pe_rowptr", ctypes.c_void_p), ("pe_col", ctypes.c_void_p), ("pe_cap", ctypes.c_int64)]
+
+
+class CrispError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libcrisp.so (built by ``dynamic_sparse_attention_proxy_amd.build``); raise if missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise CrispError(f"{path} is missing: build it with `python -m dynamic_sparse_attention_proxy_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, S, C = ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Config)
+        lib.crisp_workspace_size.argtypes = [S, C]
+        lib.crisp_workspace_size.restype = ctypes.c_size_t
+        lib.crisp_index_capacity.argtypes = [S, C]
+        lib.crisp_index_capacity.restype = ctypes.c_int64
+        lib.crisp_route.argtypes = [S, C, P, P, ctypes.POINTER(RelBias), P, ctypes.c_size_t,
+                                    ctypes.POINTER(IndexSets), P]
+        lib.crisp_route.restype = ctypes.c_int
+        lib.crisp_select_indices.argtypes = [S, C, P, P, P, ctypes.c_size_t, ctypes.POINTER(IndexSets), P]
+        lib.crisp_select_indices.restype = ctypes.c_int
+        lib.crisp_sparse_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), ctypes.POINTER(IndexSets), P,
+                                             ctypes.c_size_t, P, P]
+        lib.crisp_sparse_prefill.restype = ctypes.c_int
+        lib.crisp_dense_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), P, P]
+        lib.crisp_dense_prefill.restype = ctypes.c_int
+        lib.crisp_status_string.argtypes = [ctypes.c_int]
+        lib.crisp_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        msg = load_library().crisp_status_string(code).decode()
+        raise CrispError(f"{what}: {STATUS.get(code, code)} ({msg})")
+
+
+@dataclass
+class LayerSpec:
+    """Shape and hyper-parameters of one prefill layer."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    head_dim: int
+    dtype: int  # F32 or BF16
+    block: int = 128
+    w_sink: int = 128
+    w_local: int = 128
+    tau: tuple = (1, 10)
+    alpha: tuple = (1, 1)
+    gamma: tuple = (19, 20)
+    select_mode: int = SELECT_NOISE_FLOOR
+
+    def shape(self) -> Shape:
+        return Shape(self.batch, self.n_q_heads, self.n_kv_heads, self.seq_len, self.head_dim, self.dtype)
+
+    def config(self) -> Config:
+        return Config(self.block, self.w_sink, self.w_local, self.tau[0], self.tau[1], self.alpha[0],
+                      self.alpha[1], self.gamma[0], self.gamma[1], self.select_mode)
+
+    @property
+    def num_blocks(self) -> int:
+        return (self.seq_len + self.block - 1) // self.block
+
+    @property
+    def heads(self) -> int:
+        return self.batch * self.n_q_heads
+
+
+def workspace_size(spec: LayerSpec) -> int:
+    return int(load_library().crisp_workspace_size(ctypes.byref(spec.shape()), ctypes.byref(spec.config())))
+
+
+def index_capacity(spec: LayerSpec) -> int:
+    return int(load_library().crisp_index_capacity(ctypes.byref(spec.shape()), ctypes.byref(spec.config())))
+
+
+class Buffers:
+    """Device buffers for one layer: routing outputs, index sets and workspace (torch tensors)."""
+
+    def __init__(self, spec: LayerSpec, device="cuda"):
+        import torch
+        bh, nb = spec.heads, spec.num_blocks
+        cap = index_capacity(spec)
+        if cap < 0:
+            raise CrispError("invalid layer spec")
+        i32, i64 = torch.int32, torch.int64
+        self.spec = spec
+        self.route = torch.zeros(bh, dtype=torch.uint8, device=device)
+        self.cstruct_num = torch.zeros(bh, dtype=i64, device=device)
+        self.mass_v = torch.zeros(bh, nb, dtype=i64, device=device)
+        self.mass_s = torch.zeros(bh, nb, dtype=i64, device=device)
+        self.mass_total = torch.zeros(bh, dtype=i64, device=device)
+        self.vs_count = torch.zeros(bh, 2, dtype=i32, device=device)
+        self.vs_vertical = torch.zeros(bh, nb, dtype=i32, device=device)
+        self.vs_slash = torch.zeros(bh, nb, dtype=i32, device=device)
+        self.pe_rowptr = torch.zeros(bh, nb + 1, dtype=i32, device=device)
+        self.pe_col = torch.zeros(bh, cap, dtype=i32, device=device)
+        self.pe_cap = cap
+        self.ws_bytes = workspace_size(spec)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def index_sets(self) -> IndexSets:
+        return IndexSets(self.route.data_ptr(), self.cstruct_num.data_ptr(), self.mass_v.data_ptr(),
+                         self.mass_s.data_ptr(), self.mass_total.data_ptr(), self.vs_count.data_ptr(),
+                         self.vs_vertical.data_ptr(), self.vs_slash.data_ptr(), self.pe_rowptr.data_ptr(),
+                         self.pe_col.data_ptr(), self.pe_cap)
+
+
+def _bias(offsets, values) -> RelBias:
+    if offsets is None or offsets.numel() == 0:
+        return RelBias(0, None, None)
+    return RelBias(int(offsets.shape[-1]), offsets.data_ptr(), values.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def route(spec: LayerSpec, q, k, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):
+    """crisp_route: proxy map of the last query block, C_struct and route bits into ``bufs``."""
+    idx = bufs.index_sets()
+    b = _bias(bias_offsets, bias_values)
+    _check(load_library().crisp_route(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), q.data_ptr(),
+                                      k.data_ptr(), ctypes.byref(b), bufs.ws.data_ptr(), bufs.ws_bytes,
+                                      ctypes.byref(idx), _stream(stream)), "crisp_route")
+
+
+def select_indices(spec: LayerSpec, q, k, bufs: Buffers, stream=None):
+    """crisp_select_indices: VS block lists (Eq. 3-4) and PE block sets (Alg. 4) into ``bufs``."""
+    idx = bufs.index_sets()
+    _check(load_library().crisp_select_indices(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
+                                               q.data_ptr(), k.data_ptr(), bufs.ws.data_ptr(), bufs.ws_bytes,
+                                               ctypes.byref(idx), _stream(stream)), "crisp_select_indices")
+
+
+def sparse_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None,
+                   stream=None):
+    """crisp_sparse_prefill: attention over the selected blocks, written into ``o``."""
+    idx = bufs.index_sets()
+    b = _bias(bias_offsets, bias_values)
+    _check(load_library().crisp_sparse_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
+                                               q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(b),
+                                               ctypes.byref(idx), bufs.ws.data_ptr(), bufs.ws_bytes, o.data_ptr(),
+                                               _stream(stream)), "crisp_sparse_prefill")
+
+
+def dense_prefill(spec: LayerSpec, q, k, v, o, bias_offsets=None, bias_values=None, stream=None):
+    """crisp_dense_prefill: full causal attention with the same tile engine."""
+    b = _bias(bias_offsets, bias_values)
+    _check(load_library().crisp_dense_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
+                                              q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(b),
+                                              o.data_ptr(), _stream(stream)), "crisp_dense_prefill")
+
+
+def prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):
+    """One layer of the sparse path: route, select, sparse attention (Alg. 1)."""
+    route(spec, q, k, bufs, bias_offsets, bias_values, stream)
+    select_indices(spec, q, k, bufs, stream)
+    sparse_prefill(spec, q, k, v, o, bufs, bias_offsets, bias_values, stream)

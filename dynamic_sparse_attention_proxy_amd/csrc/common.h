@@ -1,0 +1,86 @@
+// Device-side helpers shared by the CRISP HIP kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crisp {
+
+constexpr int kFixShift = 40;  // fixed-point scale 2^40 for every decision sum
+
+typedef unsigned short bf16_t;  // storage of bfloat16 values
+
+struct bf16x8 {
+  uint4 v;
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T* p);
+template <>
+__device__ __forceinline__ float load_f32<float>(const float* p) {
+  return *p;
+}
+template <>
+__device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) {
+  return bf16_to_f32(*p);
+}
+
+// e^x for x <= 0 in fp32, bit-identical by construction to the reference
+// definition: Cody-Waite reduction x = k ln2 + r (k = rint(x log2 e), ln2 in a
+// 15-bit head and a tail), Taylor polynomial of degree 7 in Horner form with
+// coefficients 1/j! rounded to fp32, result p 2^k; 0 below -80.
+__device__ __forceinline__ float exp_crisp(float x) {
+  if (x < -80.0f) return 0.0f;
+  const float log2e = 1.44269502f;         // 0x3FB8AA3B
+  const float ln2_hi = 0.693145751953125f; // 0x3F317200
+  const float ln2_lo = 1.42860677e-06f;    // 0x35BFBE8E
+  float t = x * log2e;
+  float kf = __builtin_rintf(t);
+  float r = __builtin_fmaf(-kf, ln2_hi, x);
+  r = __builtin_fmaf(-kf, ln2_lo, r);
+  float p = 1.0f / 5040.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)kf);
+}
+
+// rne(v * 2^40) for 0 <= v <= 1: exact scaling, round half to even, exact conversion.
+__device__ __forceinline__ long long fix_rne(float v) {
+  return (long long)__builtin_rintf(__builtin_ldexpf(v, kFixShift));
+}
+
+// fl32(L) * 2^-40 (int64 -> fp32 rounds to nearest even).
+__device__ __forceinline__ float fix_to_float(long long L) {
+  return __builtin_ldexpf((float)L, -kFixShift);
+}
+
+// Order-preserving map of fp32 onto int32 (for atomicMax of floats).
+__device__ __forceinline__ int float_to_ordered(float f) {
+  int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float ordered_to_float(int o) {
+  return __int_as_float(o ^ ((o >> 31) & 0x7fffffff));
+}
+
+__device__ __forceinline__ long long shfl_xor_i64(long long v, int m) {
+  int lo = __shfl_xor((int)(v & 0xffffffff), m);
+  int hi = __shfl_xor((int)(v >> 32), m);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_i64(v, m);
+  return v;
+}
+
+}  // namespace crisp

@@ -1,0 +1,528 @@
+// Index selection (CRISP summary page, Methodology).
+//
+// VS heads, sink-aware noise floor (Eq. 3 and Eq. 4, Alg. 3): per direction
+// keep the first and last block and every middle block with
+// p_b > alpha * mu, mu = max(T - p_first - p_last, 0) / (N_b - 2), tested as
+// alpha_den (N_b - 2) p_b > alpha_num M in exact integers, compacted into
+// ascending lists with wave ballots.
+//
+// PE heads, GlobalAdaptive (Alg. 4): block means of Q and K (sequential fp32
+// sums), pooled scores zbar = fl(fma-chain(Qbar, Kbar) c) for kb <= qb, row
+// softmax with exp_crisp and int64 sums, quantised map Abar_q, total Tbar.
+// The gamma-cumsum prefix under the order (Abar_q desc, flat index asc) is
+// found by a radix select over the 41-bit values with (count, mass)
+// histograms, then ties at the cut value are taken in index order; every
+// diagonal block is added; rows are written as CSR.
+#include "common.h"
+#include "kernels.h"
+
+namespace crisp {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ long long block_sum_i64(long long v, long long* red) {
+  v = wave_sum_i64(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  long long s = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// Ascending compaction of flags over one block of threads.  Returns the
+// position of this thread's element (valid if flag) and the block total.
+__device__ __forceinline__ int block_compact(bool flag, int* wave_cnt, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const unsigned long long mask = __ballot(flag);
+  const int before = __popcll(mask & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) wave_cnt[wave] = __popcll(mask);
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) off += wave_cnt[w];
+    tot += wave_cnt[w];
+  }
+  *total = tot;
+  return off + before;
+}
+
+__global__ __launch_bounds__(kThreads) void vs_select_kernel(Dims dm, SelectArgs sa, IndexOut io) {
+  __shared__ int wave_cnt[4];
+  const int bh = blockIdx.x, tid = threadIdx.x, nb = dm.nb;
+  if (!io.route[bh]) {
+    if (tid < 2) io.vs_count[bh * 2 + tid] = 0;
+    return;
+  }
+  const long long T = io.mass_total[bh];
+  for (int dir = 0; dir < 2; ++dir) {
+    const long long* p = (dir == 0 ? io.mass_v : io.mass_s) + (size_t)bh * nb;
+    int* list = (dir == 0 ? io.vs_vertical : io.vs_slash) + (size_t)bh * nb;
+    const bool all = sa.keep_all || nb <= 2;
+    long long M = all ? 0 : T - p[0] - p[nb - 1];
+    if (M < 0) M = 0;
+    const unsigned __int128 rhs = (unsigned __int128)sa.alpha_num * (unsigned __int128)M;
+    int cnt = 0;
+    for (int base = 0; base < nb; base += kThreads) {
+      const int b = base + tid;
+      bool flag = false;
+      if (b < nb) {
+        if (all || b == 0 || b == nb - 1) {
+          flag = true;
+        } else {
+          const unsigned __int128 lhs = (unsigned __int128)sa.alpha_den *
+                                        (unsigned __int128)(nb - 2) * (unsigned __int128)p[b];
+          flag = lhs > rhs;
+        }
+      }
+      int tot;
+      const int pos = block_compact(flag, wave_cnt, &tot);
+      if (flag) list[cnt + pos] = b;
+      cnt += tot;
+    }
+    if (tid == 0) io.vs_count[bh * 2 + dir] = cnt;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- PE path ----
+__device__ __forceinline__ bool group_has_pe(const IndexOut& io, const Dims& dm, int kvh) {
+  const int b = kvh / dm.hkv, g = kvh % dm.hkv;
+  for (int t = 0; t < dm.group; ++t)
+    if (!io.route[b * dm.hq + g * dm.group + t]) return true;
+  return false;
+}
+
+// Block means: Qbar[qb][k] = fl(sum over rows ascending) / cnt; same for K.
+template <typename T>
+__global__ void pe_pool_kernel(Dims dm, const T* __restrict__ q, const T* __restrict__ k, IndexOut io,
+                               float* __restrict__ qbar, float* __restrict__ kbar) {
+  const int qb = blockIdx.x, y = blockIdx.y, kk = threadIdx.x;
+  const T* src;
+  float* dst;
+  if (y < dm.bh) {
+    if (io.route[y]) return;
+    src = q + (size_t)y * dm.n * dm.d;
+    dst = qbar + ((size_t)y * dm.nb + qb) * dm.d;
+  } else {
+    const int kvh = y - dm.bh;
+    if (!group_has_pe(io, dm, kvh)) return;
+    src = k + (size_t)kvh * dm.n * dm.d;
+    dst = kbar + ((size_t)kvh * dm.nb + qb) * dm.d;
+  }
+  const int r0 = qb * dm.B;
+  const int cnt = min(dm.B, dm.n - r0);
+  float s = 0.0f;
+  for (int r = 0; r < cnt; ++r) s = s + load_f32(src + (size_t)(r0 + r) * dm.d + kk);
+  dst[kk] = s / (float)cnt;
+}
+
+// Pooled scores, 64 x 64 tile per block, 4 x 4 per thread, chunk of 32 over d.
+template <int D>
+__global__ __launch_bounds__(kThreads) void pe_scores_kernel(Dims dm, IndexOut io,
+                                                             const float* __restrict__ qbar,
+                                                             const float* __restrict__ kbar,
+                                                             float* __restrict__ zbar) {
+  constexpr int TL = 64, TM = 4, KC = 32, LD = TL + 4;
+  __shared__ __align__(16) float Qs[KC * LD];
+  __shared__ __align__(16) float Ks[KC * LD];
+  const int rt = blockIdx.x, ct = blockIdx.y, bh = blockIdx.z, tid = threadIdx.x;
+  if (ct > rt || io.route[bh]) return;
+  const int ty = tid & 15, tx = tid >> 4;
+  const int b = bh / dm.hq;
+  const int kvh = b * dm.hkv + (bh % dm.hq) / dm.group;
+  const float* qs = qbar + (size_t)bh * dm.nb * D;
+  const float* ks = kbar + (size_t)kvh * dm.nb * D;
+  float acc[TM][TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = 0.0f;
+  for (int dc = 0; dc < D; dc += KC) {
+    for (int e = tid; e < TL * KC; e += kThreads) {
+      const int r = e / KC, kk = e % KC;
+      const int qr = rt * TL + r, kr = ct * TL + r;
+      Qs[kk * LD + r] = qr < dm.nb ? qs[(size_t)qr * D + dc + kk] : 0.0f;
+      Ks[kk * LD + r] = kr < dm.nb ? ks[(size_t)kr * D + dc + kk] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < KC; ++kk) {
+      const float4 va = *reinterpret_cast<const float4*>(&Qs[kk * LD + ty * TM]);
+      const float4 vb = *reinterpret_cast<const float4*>(&Ks[kk * LD + tx * TM]);
+      const float a[4] = {va.x, va.y, va.z, va.w};
+      const float bb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const float c = (float)(1.0 / __builtin_sqrt((double)D));
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int qb = rt * TL + ty * TM + i;
+    if (qb >= dm.nb) continue;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int kb = ct * TL + tx * TM + j;
+      if (kb <= qb) zbar[((size_t)bh * dm.nb + qb) * dm.nb + kb] = acc[i][j] * c;
+    }
+  }
+}
+
+__device__ __forceinline__ float block_max_f32(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = red[w] > r ? red[w] : r;
+  __syncthreads();
+  return r;
+}
+
+// Row softmax of the pooled map in fixed point: Abar_q row, row total.
+__global__ __launch_bounds__(kThreads) void pe_rowsoft_kernel(Dims dm, IndexOut io,
+                                                              const float* __restrict__ zbar,
+                                                              long long* __restrict__ abar,
+                                                              long long* __restrict__ rowtot) {
+  __shared__ float redf[4];
+  __shared__ long long redi[4];
+  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  if (io.route[bh]) return;
+  const float* z = zbar + ((size_t)bh * dm.nb + qb) * dm.nb;
+  float m = -__builtin_inff();
+  for (int kb = tid; kb <= qb; kb += kThreads) m = z[kb] > m ? z[kb] : m;
+  m = block_max_f32(m, redf);
+  long long L = 0;
+  for (int kb = tid; kb <= qb; kb += kThreads) L += fix_rne(exp_crisp(z[kb] - m));
+  L = block_sum_i64(L, redi);
+  const float l = fix_to_float(L);
+  long long* out = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
+  long long tot = 0;
+  for (int kb = tid; kb <= qb; kb += kThreads) {
+    const long long aq = fix_rne(exp_crisp(z[kb] - m) / l);
+    out[kb] = aq;
+    tot += aq;
+  }
+  tot = block_sum_i64(tot, redi);
+  if (tid == 0) rowtot[(size_t)bh * dm.nb + qb] = tot;
+}
+
+// Radix-select state per head (int64 slots):
+//   0 remaining mass R still to cover inside the current prefix
+//   1 value prefix found so far
+//   2 cut value v* (set after the last pass; -1 = keep all; INT64_MAX = keep none)
+//   3 number of ties at v* to take (in index order)
+//   4 active flag
+constexpr int kPassShift[4] = {30, 20, 10, 0};
+constexpr int kPassWidth[4] = {11, 10, 10, 10};
+constexpr int kHistBins = 2048;
+
+__global__ __launch_bounds__(kThreads) void pe_radix_init_kernel(Dims dm, SelectArgs sa, IndexOut io,
+                                                                 const long long* __restrict__ rowtot,
+                                                                 unsigned long long* __restrict__ hist,
+                                                                 long long* __restrict__ state) {
+  __shared__ long long red[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  long long* st = state + (size_t)bh * 8;
+  if (io.route[bh]) return;
+  if (sa.keep_all) {
+    if (tid == 0) st[0] = 0, st[1] = 0, st[2] = -1, st[3] = 0, st[4] = 0;
+    return;
+  }
+  unsigned long long* h = hist + (size_t)bh * 4 * kHistBins * 2;
+  for (int i = tid; i < 4 * kHistBins * 2; i += kThreads) h[i] = 0;
+  long long T = 0;
+  for (int qb = tid; qb < dm.nb; qb += kThreads) T += rowtot[(size_t)bh * dm.nb + qb];
+  T = block_sum_i64(T, red);
+  if (tid == 0) {
+    // target: smallest integer cum with gamma_den cum >= gamma_num T
+    const unsigned __int128 num = (unsigned __int128)sa.gamma_num * (unsigned __int128)T;
+    const unsigned __int128 tgt = (num + sa.gamma_den - 1) / sa.gamma_den;
+    st[0] = (long long)tgt;
+    st[1] = 0;
+    st[2] = tgt == 0 ? 0x7fffffffffffffffLL : 0;
+    st[3] = 0;
+    st[4] = tgt == 0 ? 0 : 1;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void pe_radix_hist_kernel(Dims dm, IndexOut io, int pass,
+                                                                 const long long* __restrict__ abar,
+                                                                 unsigned long long* __restrict__ hist,
+                                                                 const long long* __restrict__ state,
+                                                                 long long chunk) {
+  __shared__ unsigned int cnt[kHistBins];
+  __shared__ unsigned long long mass[kHistBins];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  if (io.route[bh] || !state[(size_t)bh * 8 + 4]) return;
+  const long long begin = (long long)blockIdx.x * chunk;
+  if (begin >= dm.ntri) return;
+  const long long end = min(begin + chunk, dm.ntri);
+  const int shift = kPassShift[pass], width = kPassWidth[pass];
+  const long long prefix = state[(size_t)bh * 8 + 1];
+  const int hi = shift + width;
+  for (int i = tid; i < kHistBins; i += kThreads) cnt[i] = 0, mass[i] = 0;
+  __syncthreads();
+  const long long* a = abar + (size_t)bh * dm.ntri;
+  for (long long e = begin + tid; e < end; e += kThreads) {
+    const long long v = a[e];
+    if ((v >> hi) == (prefix >> hi)) {
+      const int dg = (int)((v >> shift) & ((1 << width) - 1));
+      atomicAdd(&cnt[dg], 1u);
+      atomicAdd(&mass[dg], (unsigned long long)v);
+    }
+  }
+  __syncthreads();
+  unsigned long long* h = hist + ((size_t)bh * 4 + pass) * kHistBins * 2;
+  for (int i = tid; i < (1 << width); i += kThreads) {
+    if (cnt[i]) {
+      atomicAdd(&h[2 * i], (unsigned long long)cnt[i]);
+      atomicAdd(&h[2 * i + 1], mass[i]);
+    }
+  }
+}
+
+// Find the digit where the running mass (from the largest values down) first
+// reaches the remaining target R; everything in higher buckets is inside the
+// prefix.  After the last pass the full cut value v* is known.
+__global__ __launch_bounds__(kThreads) void pe_radix_scan_kernel(Dims dm, IndexOut io, int pass,
+                                                                 const unsigned long long* __restrict__ hist,
+                                                                 long long* __restrict__ state) {
+  __shared__ long long part[kThreads];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  long long* st = state + (size_t)bh * 8;
+  if (io.route[bh] || !st[4]) return;
+  const int shift = kPassShift[pass], width = kPassWidth[pass];
+  const int bins = 1 << width;
+  const int per = bins / kThreads;  // 8 or 4 digits per thread, highest digits to thread 0
+  const unsigned long long* h = hist + ((size_t)bh * 4 + pass) * kHistBins * 2;
+  const long long R = st[0];
+  long long mine = 0;
+  for (int t = 0; t < per; ++t) mine += (long long)h[2 * (bins - 1 - (tid * per + t)) + 1];
+  part[tid] = mine;
+  __syncthreads();
+  // exclusive prefix (Hillis-Steele) over threads in descending-digit order
+  for (int off = 1; off < kThreads; off <<= 1) {
+    long long v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const long long before = part[tid] - mine;
+  if (before < R && R <= before + mine) {
+    long long cum = before;
+    for (int t = 0; t < per; ++t) {
+      const int dg = bins - 1 - (tid * per + t);
+      const long long s = (long long)h[2 * dg + 1];
+      if (cum + s >= R) {
+        const long long prefix = st[1] | ((long long)dg << shift);
+        const long long Rn = R - cum;
+        st[0] = Rn;
+        st[1] = prefix;
+        if (pass == 3) {
+          st[2] = prefix;                  // v* (> 0 since Rn > 0)
+          st[3] = (Rn + prefix - 1) / prefix;  // ties at v* needed, lowest indices first
+        }
+        break;
+      }
+      cum += s;
+    }
+  }
+}
+
+// Per query-block row: values above v*, ties at v*.
+__global__ __launch_bounds__(kThreads) void pe_count_kernel(Dims dm, IndexOut io,
+                                                            const long long* __restrict__ abar,
+                                                            const long long* __restrict__ state,
+                                                            int* __restrict__ gtcnt, int* __restrict__ tiecnt) {
+  __shared__ int red[8];
+  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  if (io.route[bh]) return;
+  const long long vstar = state[(size_t)bh * 8 + 2];
+  const long long* a = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
+  int gt = 0, tie = 0;
+  if (vstar >= 0 && vstar != 0x7fffffffffffffffLL)
+    for (int kb = tid; kb <= qb; kb += kThreads) {
+      gt += a[kb] > vstar;
+      tie += a[kb] == vstar;
+    }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    gt += __shfl_xor(gt, m);
+    tie += __shfl_xor(tie, m);
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = gt, red[4 + (tid >> 6)] = tie;
+  __syncthreads();
+  if (tid == 0) {
+    gtcnt[(size_t)bh * dm.nb + qb] = red[0] + red[1] + red[2] + red[3];
+    tiecnt[(size_t)bh * dm.nb + qb] = red[4] + red[5] + red[6] + red[7];
+  }
+}
+
+// Row pointers: exclusive scans over query blocks of the tie counts and the
+// row sizes (values above v*, the first ties, plus the diagonal if not in).
+__global__ __launch_bounds__(1024) void pe_scan_kernel(Dims dm, IndexOut io,
+                                                       const long long* __restrict__ abar,
+                                                       const long long* __restrict__ state,
+                                                       const int* __restrict__ gtcnt,
+                                                       const int* __restrict__ tiecnt,
+                                                       int* __restrict__ tiepre) {
+  __shared__ long long sa[1024], sb[1024];
+  const int bh = blockIdx.x, tid = threadIdx.x, nb = dm.nb;
+  int* rowptr = io.pe_rowptr + (size_t)bh * (nb + 1);
+  if (io.route[bh]) {
+    for (int i = tid; i <= nb; i += 1024) rowptr[i] = 0;
+    return;
+  }
+  const long long* st = state + (size_t)bh * 8;
+  const long long vstar = st[2], rties = st[3];
+  const bool all = vstar < 0;
+  const int per = (nb + 1023) / 1024;
+  const int lo = min(tid * per, nb), hi = min(lo + per, nb);
+  long long tsum = 0, rsum = 0;
+  for (int qb = lo; qb < hi; ++qb) {
+    tsum += all ? 0 : tiecnt[(size_t)bh * nb + qb];
+  }
+  sa[tid] = tsum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    long long v = tid >= off ? sa[tid - off] : 0;
+    __syncthreads();
+    sa[tid] += v;
+    __syncthreads();
+  }
+  long long tp = sa[tid] - tsum;  // ties in rows before lo
+  // row sizes
+  long long tcur = tp;
+  for (int qb = lo; qb < hi; ++qb) {
+    long long sz;
+    if (all) {
+      sz = qb + 1;
+    } else {
+      const int tc = tiecnt[(size_t)bh * nb + qb];
+      long long take = rties - tcur;
+      take = take < 0 ? 0 : (take > tc ? tc : take);
+      const long long vd = abar[(size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2 + qb];
+      // the diagonal is the last element of its row: if it ties, it has the row's last tie rank
+      const bool diag_in = vd > vstar || (vd == vstar && tcur + tc - 1 < rties);
+      sz = gtcnt[(size_t)bh * nb + qb] + take + (diag_in ? 0 : 1);
+      tiepre[(size_t)bh * nb + qb] = (int)tcur;
+      tcur += tc;
+    }
+    rsum += sz;
+  }
+  sb[tid] = rsum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    long long v = tid >= off ? sb[tid - off] : 0;
+    __syncthreads();
+    sb[tid] += v;
+    __syncthreads();
+  }
+  long long rp = sb[tid] - rsum;
+  tcur = tp;
+  for (int qb = lo; qb < hi; ++qb) {
+    rowptr[qb] = (int)rp;
+    long long sz;
+    if (all) {
+      sz = qb + 1;
+    } else {
+      const int tc = tiecnt[(size_t)bh * nb + qb];
+      long long take = rties - tcur;
+      take = take < 0 ? 0 : (take > tc ? tc : take);
+      const long long vd = abar[(size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2 + qb];
+      const bool diag_in = vd > vstar || (vd == vstar && tcur + tc - 1 < rties);
+      sz = gtcnt[(size_t)bh * nb + qb] + take + (diag_in ? 0 : 1);
+      tcur += tc;
+    }
+    rp += sz;
+  }
+  if (tid == 1023) rowptr[nb] = (int)rp;
+}
+
+__global__ __launch_bounds__(kThreads) void pe_write_kernel(Dims dm, IndexOut io,
+                                                            const long long* __restrict__ abar,
+                                                            const long long* __restrict__ state,
+                                                            const int* __restrict__ tiepre) {
+  __shared__ int wave_cnt[4];
+  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  if (io.route[bh]) return;
+  const long long* st = state + (size_t)bh * 8;
+  const long long vstar = st[2], rties = st[3];
+  const bool all = vstar < 0;
+  const long long* a = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
+  int* out = io.pe_col + (size_t)bh * io.pe_cap + io.pe_rowptr[(size_t)bh * (dm.nb + 1) + qb];
+  long long tcur = all ? 0 : tiepre[(size_t)bh * dm.nb + qb];
+  int cnt = 0;
+  for (int base = 0; base <= qb; base += kThreads) {
+    const int kb = base + tid;
+    const bool in = kb <= qb;
+    const long long v = (in && !all) ? a[kb] : 0;
+    const bool tie = in && !all && v == vstar;
+    int ntie;
+    const int tpos = block_compact(tie, wave_cnt, &ntie);
+    bool flag = in && (all || v > vstar || kb == qb || (tie && tcur + tpos < rties));
+    tcur += ntie;
+    int tot;
+    const int pos = block_compact(flag, wave_cnt, &tot);
+    if (flag) out[cnt + pos] = kb;
+    cnt += tot;
+  }
+}
+
+template <typename T>
+void launch_pool(const Dims& dm, const void* q, const void* k, const IndexOut& io, float* qbar,
+                 float* kbar, hipStream_t st) {
+  pe_pool_kernel<T><<<dim3(dm.nb, dm.bh + dm.bkv), dm.d, 0, st>>>(
+      dm, static_cast<const T*>(q), static_cast<const T*>(k), io, qbar, kbar);
+}
+
+}  // namespace
+
+hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, const void* k,
+                         const SelectScratch& ws, const IndexOut& io, hipStream_t st) {
+  vs_select_kernel<<<dm.bh, kThreads, 0, st>>>(dm, sa, io);
+  if (!sa.keep_all) {
+    if (dm.dtype == 1)
+      launch_pool<bf16_t>(dm, q, k, io, ws.qbar, ws.kbar, st);
+    else
+      launch_pool<float>(dm, q, k, io, ws.qbar, ws.kbar, st);
+    const int nt = (dm.nb + 63) / 64;
+    if (dm.d == 128)
+      pe_scores_kernel<128><<<dim3(nt, nt, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
+    else
+      pe_scores_kernel<64><<<dim3(nt, nt, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
+    pe_rowsoft_kernel<<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, io, ws.zbar, ws.abar, ws.rowtot);
+  }
+  pe_radix_init_kernel<<<dm.bh, kThreads, 0, st>>>(dm, sa, io, ws.rowtot, ws.hist, ws.state);
+  if (!sa.keep_all) {
+    const long long chunk = 16384;
+    const int nchunks = (int)((dm.ntri + chunk - 1) / chunk);
+    for (int pass = 0; pass < 4; ++pass) {
+      pe_radix_hist_kernel<<<dim3(nchunks, dm.bh), kThreads, 0, st>>>(dm, io, pass, ws.abar, ws.hist,
+                                                                        ws.state, chunk);
+      pe_radix_scan_kernel<<<dm.bh, kThreads, 0, st>>>(dm, io, pass, ws.hist, ws.state);
+    }
+    pe_count_kernel<<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.gtcnt,
+                                                             ws.tiecnt);
+  }
+  pe_scan_kernel<<<dm.bh, 1024, 0, st>>>(dm, io, ws.abar, ws.state, ws.gtcnt, ws.tiecnt, ws.tiepre);
+  pe_write_kernel<<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.tiepre);
+  return hipGetLastError();
+}
+
+}  // namespace crisp

@@ -63,7 +63,7 @@ def _load():
         lib.oracle_vs_select.restype = i32
         lib.oracle_cumulative_select.argtypes = [i64, P, i64, u32, u32, P]
         lib.oracle_cumulative_select.restype = i32
-        lib.oracle_pe_index.argtypes = [i64, i32, i32, P, P, u32, u32, P, P, P, P]
+        lib.oracle_pe_index.argtypes = [i64, i32, i32, P, P, u32, u32, P, P, P, P, i32]
         lib.oracle_pe_index.restype = i64
         lib.oracle_attention_row.argtypes = [i64, i32, P, P, P, i32, P, P, P, P]
         lib.oracle_attention_row.restype = None
@@ -153,7 +153,7 @@ def cumulative_select(p, total, gamma=(19, 20)) -> np.ndarray:
     return out[:c].copy()
 
 
-def pe_index(qh, kh, B, gamma=(19, 20), want_abar=False):
+def pe_index(qh, kh, B, gamma=(19, 20), want_abar=False, threads=0):
     """Alg. 4 (GlobalAdaptive) for one query head.
 
     Returns (rowptr, cols) or, with want_abar, (rowptr, cols, Abar_q, Tbar, prefix_len)."""
@@ -168,7 +168,7 @@ def pe_index(qh, kh, B, gamma=(19, 20), want_abar=False):
     abar = np.zeros(ntri, np.int64) if want_abar else None
     tbar = np.zeros(2, np.int64)
     nnz = lib.oracle_pe_index(n, d, B, _p(qh), _p(kh), gamma[0], gamma[1], _p(rowptr), _p(cols),
-                              _p(abar), _p(tbar))
+                              _p(abar), _p(tbar), threads)
     cols = cols[:nnz].copy()
     if want_abar:
         return rowptr, cols, abar, int(tbar[0]), int(tbar[1])
@@ -187,6 +187,16 @@ def index_sets(q, k, B, w_sink, w_local, tau=(1, 10), alpha=(1, 1), gamma=(19, 2
     bh = q.shape[0]
     G = bh // k.shape[0]
     nb = pr["nb"]
+    pe_heads = [h for h in range(bh) if not pr["route"][h]]
+    pe_out = {}
+    if not keep_all and pe_heads:
+        # independent heads in parallel threads (the C routine releases the GIL)
+        import concurrent.futures as cf
+        workers = max(1, min(len(pe_heads), os.cpu_count() or 1, 16))
+        with cf.ThreadPoolExecutor(workers) as ex:
+            futs = {h: ex.submit(pe_index, q[h], k[h // G], B, gamma, False, 1 if workers > 1 else 0)
+                    for h in pe_heads}
+            pe_out = {h: f.result() for h, f in futs.items()}
     heads = []
     for h in range(bh):
         if pr["route"][h]:
@@ -202,7 +212,7 @@ def index_sets(q, k, B, w_sink, w_local, tau=(1, 10), alpha=(1, 1), gamma=(19, 2
                 rowptr = np.concatenate([[0], np.cumsum(np.arange(1, nb + 1))]).astype(np.int32)
                 cols = np.concatenate([np.arange(qb + 1) for qb in range(nb)]).astype(np.int32)
             else:
-                rowptr, cols = pe_index(q[h], k[h // G], B, gamma)
+                rowptr, cols = pe_out[h]
             heads.append(dict(route=0, rowptr=rowptr, cols=cols))
     return dict(proxy=pr, heads=heads)
 
@@ -222,7 +232,7 @@ def _allowed(spec, rows, j, B, nb):
         ins = torch.zeros(nb, dtype=torch.bool)
         ins[torch.as_tensor(spec["slash"], dtype=torch.long)] = True
         vert = inv[j // B][None, :]
-        sl = ins[torch.clamp(o, min=0) // B]
+        sl = ins[torch.div(torch.clamp(o, min=0).to(torch.int32), B, rounding_mode="floor").long()]
         return causal & (vert | sl)
     if kind == "pe":
         keep = spec.get("_keep")
@@ -236,24 +246,26 @@ def _allowed(spec, rows, j, B, nb):
     raise ValueError(kind)
 
 
-def attention(q, k, v, B, specs, rows=None, bias_offsets=None, bias_values=None, chunk=256):
+def attention(q, k, v, B, specs, rows=None, bias_offsets=None, bias_values=None, chunk=256, heads=None):
     """Masked causal attention in fp64 (plain PyTorch CPU ops).
 
     q [bh, n, d], k/v [bkv, n, d] (float32 values).  specs: one dict per query
     head, {"kind": "dense"} or {"kind": "vs", "vertical", "slash"} or
     {"kind": "pe", "rowptr", "cols"}.  rows: query rows to evaluate (default
-    all).  Returns float64 [bh, len(rows), d].
+    all); heads: query heads to evaluate (default all).  Returns float64
+    [len(heads), len(rows), d].
     """
     import torch
     bh, n, d = q.shape
     G = bh // k.shape[0]
     nb = num_blocks(n, B)
     rows = np.arange(n) if rows is None else np.asarray(rows)
+    heads = list(range(bh)) if heads is None else list(heads)
     rows_t = torch.as_tensor(rows, dtype=torch.long)
-    out = torch.empty((bh, len(rows), d), dtype=torch.float64)
+    out = torch.empty((len(heads), len(rows), d), dtype=torch.float64)
     c = 1.0 / np.sqrt(d)
     kv_cache = {}
-    for h in range(bh):
+    for hi, h in enumerate(heads):
         g = h // G
         if g not in kv_cache:
             kv_cache.clear()
@@ -268,14 +280,16 @@ def attention(q, k, v, B, specs, rows=None, bias_offsets=None, bias_values=None,
             j = torch.arange(jmax)
             S = (qh[r].double() @ K[:jmax].T) * c
             if has_bias:
-                o = r[:, None] - j[None, :]
+                # logit(i, j) += value where i - j == offset: one entry per row
                 for off, val in zip(bias_offsets[h], bias_values[h]):
-                    if val != 0:
-                        S = S + float(val) * (o == int(off)).double()
+                    if val != 0 and off >= 0:
+                        jj = r - int(off)
+                        ok = (jj >= 0) & (jj < jmax)
+                        S[torch.nonzero(ok).ravel(), jj[ok]] += float(val)
             mask = _allowed(specs[h], r, j, B, nb)
             S = S.masked_fill(~mask, float("-inf"))
             P = torch.softmax(S, dim=1)
-            out[h, s:s + chunk] = P @ V[:jmax]
+            out[hi, s:s + chunk] = P @ V[:jmax]
     return out.numpy()
 
 

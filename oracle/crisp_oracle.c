@@ -27,6 +27,7 @@
  * Build: gcc -O2 -ffp-contract=off (no contraction, no fast-math).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -271,7 +272,7 @@ int32_t oracle_cumulative_select(int64_t nb, const int64_t* p, int64_t T, uint32
  * diagonal blocks are added). */
 int64_t oracle_pe_index(int64_t n, int32_t d, int32_t B, const float* Qh, const float* Kh,
                         uint32_t g_num, uint32_t g_den, int32_t* rowptr, int32_t* cols,
-                        int64_t* Abar_out, int64_t* stats_out) {
+                        int64_t* Abar_out, int64_t* stats_out, int32_t threads) {
   const int64_t nb = (n + B - 1) / B;
   const float c = oracle_scale(d);
   float* Qb = (float*)malloc(sizeof(float) * nb * d);
@@ -292,7 +293,7 @@ int64_t oracle_pe_index(int64_t n, int32_t d, int32_t B, const float* Qh, const 
   const int64_t ntri = nb * (nb + 1) / 2;
   keyed* all = (keyed*)malloc(sizeof(keyed) * ntri);
   int64_t Tbar = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(threads > 0 ? threads : omp_get_max_threads())
   {
     float* z = (float*)malloc(sizeof(float) * nb);
     float* e = (float*)malloc(sizeof(float) * nb);

@@ -1,0 +1,139 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the C-ABI path,
+download its outputs in the oracle's formats.  Only argument marshalling here."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import dynamic_sparse_attention_proxy_amd as crisp
+import synth
+
+
+def log(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def spec_for(wl: synth.Workload, select_mode=crisp.SELECT_NOISE_FLOOR, block=None) -> crisp.LayerSpec:
+    B = block or wl.block
+    return crisp.LayerSpec(batch=wl.batch, n_q_heads=wl.hq, n_kv_heads=wl.hkv, seq_len=wl.n, head_dim=wl.d,
+                           dtype=crisp.BF16 if wl.dtype == "bf16" else crisp.F32, block=B, w_sink=B, w_local=B,
+                           tau=synth.TAU, alpha=synth.ALPHA, gamma=synth.GAMMA, select_mode=select_mode)
+
+
+class DeviceInputs:
+    def __init__(self, I: synth.Inputs, device="cuda"):
+        import torch
+        dt = torch.bfloat16 if I.wl.dtype == "bf16" else torch.float32
+
+        def up(a):
+            if a is None:
+                return None
+            t = torch.from_numpy(a).to(device)
+            return t.to(dt).contiguous() if dt != torch.float32 else t.contiguous()
+
+        self.q = up(I.q)
+        self.k = up(I.k)
+        self.v = up(I.v)
+        if I.bias_offsets.size:
+            self.bias_offsets = torch.from_numpy(I.bias_offsets).to(device).contiguous()
+            self.bias_values = torch.from_numpy(I.bias_values).to(device).contiguous()
+        else:
+            self.bias_offsets = self.bias_values = None
+        torch.cuda.synchronize()
+
+
+def run_route_select(spec, X: DeviceInputs, bufs: crisp.Buffers = None):
+    import torch
+    bufs = bufs or crisp.Buffers(spec)
+    crisp.route(spec, X.q, X.k, bufs, X.bias_offsets, X.bias_values)
+    crisp.select_indices(spec, X.q, X.k, bufs)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def download_index_sets(bufs: crisp.Buffers):
+    """GPU routing outputs and index sets in the oracle's formats."""
+    route = bufs.route.cpu().numpy()
+    out = dict(route=route, cnum=bufs.cstruct_num.cpu().numpy(), mass_v=bufs.mass_v.cpu().numpy(),
+               mass_s=bufs.mass_s.cpu().numpy(), total=bufs.mass_total.cpu().numpy())
+    cnt = bufs.vs_count.cpu().numpy()
+    vv = bufs.vs_vertical.cpu().numpy()
+    ss = bufs.vs_slash.cpu().numpy()
+    rp = bufs.pe_rowptr.cpu().numpy()
+    heads = []
+    nnz = rp[:, -1]
+    cols_all = bufs.pe_col[:, : int(nnz.max()) if nnz.size else 0].cpu().numpy()
+    for h in range(len(route)):
+        if route[h]:
+            heads.append(dict(route=1, vertical=vv[h, : cnt[h, 0]], slash=ss[h, : cnt[h, 1]], count=cnt[h]))
+        else:
+            heads.append(dict(route=0, rowptr=rp[h], cols=cols_all[h, : rp[h, -1]], count=cnt[h]))
+    out["heads"] = heads
+    return out
+
+
+def compare_index_sets(gpu, ref):
+    """Bit-exact comparison of routing outputs and index sets; returns a list of mismatch strings."""
+    bad = []
+    pr = ref["proxy"]
+    for key, rk in (("route", "route"), ("cnum", "cnum"), ("mass_v", "mass_v"), ("mass_s", "mass_s"),
+                    ("total", "total")):
+        if not np.array_equal(gpu[key], pr[rk]):
+            diff = np.argwhere(np.asarray(gpu[key] != pr[rk]))
+            bad.append(f"{key}: {len(diff)} differences, first at {diff[:3].tolist()}")
+    for h, (g, r) in enumerate(zip(gpu["heads"], ref["heads"])):
+        if g["route"] != r["route"]:
+            continue
+        if r["route"]:
+            if not np.array_equal(g["vertical"], r["vertical"]):
+                bad.append(f"head {h} vertical: gpu {g['vertical'][:10]}.. ({len(g['vertical'])}) "
+                           f"oracle {r['vertical'][:10]}.. ({len(r['vertical'])})")
+            if not np.array_equal(g["slash"], r["slash"]):
+                bad.append(f"head {h} slash: gpu {g['slash'][:10]} oracle {r['slash'][:10]}")
+        else:
+            if not np.array_equal(g["rowptr"], r["rowptr"]):
+                d = np.argwhere(g["rowptr"] != r["rowptr"])
+                bad.append(f"head {h} rowptr differs at {d[:3].ravel().tolist()} "
+                           f"(nnz gpu {g['rowptr'][-1]} oracle {r['rowptr'][-1]})")
+            elif not np.array_equal(g["cols"], r["cols"]):
+                bad.append(f"head {h} cols differ")
+    return bad
+
+
+def run_sparse(spec, X: DeviceInputs, bufs: crisp.Buffers):
+    import torch
+    o = torch.empty_like(X.q)
+    crisp.sparse_prefill(spec, X.q, X.k, X.v, o, bufs, X.bias_offsets, X.bias_values)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_dense(spec, X: DeviceInputs):
+    import torch
+    o = torch.empty_like(X.q)
+    crisp.dense_prefill(spec, X.q, X.k, X.v, o, X.bias_offsets, X.bias_values)
+    torch.cuda.synchronize()
+    return o
+
+
+def rows_of(o, rows=None):
+    import torch
+    if rows is None:
+        return o.float().cpu().numpy()
+    return o[:, torch.as_tensor(rows, device=o.device)].float().cpu().numpy()
+
+
+class Timer:
+    def __init__(self, what):
+        self.what = what
+
+    def __enter__(self):
+        self.t = time.time()
+        log("start", self.what)
+        return self
+
+    def __exit__(self, *a):
+        log("done", self.what, f"{time.time() - self.t:.1f}s")

@@ -1,0 +1,111 @@
+"""C-ABI contract on the CPU: the built library exports every call the header
+declares, and argument validation returns its error codes without touching a
+GPU (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_proxy_amd as crisp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "crisp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(crisp.LIB_PATH):
+        from dynamic_sparse_attention_proxy_amd import build
+        build.build()
+    return crisp.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(crisp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("crisp_route", "crisp_select_indices", "crisp_sparse_prefill", "crisp_dense_prefill"):
+        assert n in names
+    assert sorted(crisp.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _spec(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, seq_len=1000, head_dim=128, dtype=crisp.BF16, block=128,
+                w_sink=128, w_local=128)
+    base.update(kw)
+    return crisp.LayerSpec(**base)
+
+
+def test_sizes(lib):
+    s = _spec()
+    nb = 8
+    assert crisp.index_capacity(s) == nb * (nb + 1) // 2
+    ws = crisp.workspace_size(s)
+    assert ws >= 4 * nb * 128 * 128 * 4  # proxy tiles of every head
+    assert crisp.workspace_size(_spec(head_dim=96)) == 0
+    assert crisp.index_capacity(_spec(n_q_heads=3)) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -2), (dict(n_q_heads=6, n_kv_heads=4), -2), (dict(seq_len=0), -2),
+    (dict(seq_len=(1 << 23) + 1), -2), (dict(dtype=7), -3), (dict(block=32), -4), (dict(w_sink=0), -4),
+    (dict(tau=(1, 0)), -4), (dict(alpha=(1, 0)), -4), (dict(gamma=(3, 2)), -4), (dict(select_mode=5), -4),
+])
+def test_validation_errors(lib, kw, code):
+    s = _spec(**kw)
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced on the host
+    idx = crisp.IndexSets(*([1 << 20] * 10), 1 << 20)
+    rc = lib.crisp_route(ctypes.byref(s.shape()), ctypes.byref(s.config()), fake, fake, None, fake, 1 << 40,
+                         ctypes.byref(idx), None)
+    assert rc == code
+    rc = lib.crisp_dense_prefill(ctypes.byref(s.shape()), ctypes.byref(s.config()), fake, fake, fake, None, fake,
+                                 None)
+    assert rc == code
+
+
+def test_null_alignment_workspace_capacity(lib):
+    s = _spec()
+    sh, cf = ctypes.byref(s.shape()), ctypes.byref(s.config())
+    fake = ctypes.c_void_p(1 << 20)
+    cap = crisp.index_capacity(s)
+    ws = crisp.workspace_size(s)
+    idx = crisp.IndexSets(*([1 << 20] * 10), cap)
+    assert lib.crisp_route(None, cf, fake, fake, None, fake, ws, ctypes.byref(idx), None) == -1
+    assert lib.crisp_route(sh, cf, None, fake, None, fake, ws, ctypes.byref(idx), None) == -1
+    assert lib.crisp_route(sh, cf, ctypes.c_void_p((1 << 20) + 2), fake, None, fake, ws, ctypes.byref(idx),
+                           None) == -8
+    assert lib.crisp_route(sh, cf, fake, fake, None, fake, ws - 1, ctypes.byref(idx), None) == -5
+    nullidx = crisp.IndexSets(*([1 << 20] * 4), None, *([1 << 20] * 5), cap)
+    assert lib.crisp_route(sh, cf, fake, fake, None, fake, ws, ctypes.byref(nullidx), None) == -1
+    small = crisp.IndexSets(*([1 << 20] * 10), cap - 1)
+    assert lib.crisp_select_indices(sh, cf, fake, fake, fake, ws, ctypes.byref(small), None) == -6
+    bad_bias = crisp.RelBias(9, 1 << 20, 1 << 20)
+    assert lib.crisp_route(sh, cf, fake, fake, ctypes.byref(bad_bias), fake, ws, ctypes.byref(idx), None) == -4
+    nb = crisp.RelBias(2, None, 1 << 20)
+    assert lib.crisp_sparse_prefill(sh, cf, fake, fake, fake, ctypes.byref(nb), ctypes.byref(idx), fake, ws, fake,
+                                    None) == -1
+
+
+def test_status_strings(lib):
+    for code in range(-8, 1):
+        assert lib.crisp_status_string(code)
+    assert lib.crisp_status_string(-99) == b"unknown status"
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "dynamic_sparse_attention_proxy_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text and "liboracle" not in text, f

@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Bar: routing outputs (route bits, C_struct numerator, block masses, totals)
+and index sets bit-exact; attention max-abs 2e-2 for bf16 and 1e-5 for fp32
+against the fp64 oracle on the same index sets.  Below 128K every row is
+checked; at 128K and above the full index sets plus 256 seeded rows per head.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import dynamic_sparse_attention_proxy_amd as crisp
+import oracle
+import synth
+from gpu_harness import (DeviceInputs, Timer, compare_index_sets, download_index_sets, log, rows_of,
+                         run_dense, run_route_select, run_sparse, spec_for)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+_cache = {}
+
+
+def _case(name, wl=None, select_mode=crisp.SELECT_NOISE_FLOOR):
+    key = (name, select_mode)
+    if key in _cache:
+        return _cache[key]
+    _cache.clear()
+    gc.collect()
+    wl = wl or synth.WORKLOADS[name]
+    log("case", name, "mode", select_mode, "n", wl.n, "heads", wl.hq, wl.hkv, "d", wl.d, wl.dtype)
+    with Timer(f"inputs {name}"):
+        I = synth.make_inputs(wl)
+    with Timer(f"upload {name}"):
+        X = DeviceInputs(I)
+    spec = spec_for(wl, select_mode)
+    with Timer(f"gpu route+select {name}"):
+        bufs = run_route_select(spec, X)
+    with Timer(f"oracle index sets {name}"):
+        ref = oracle.index_sets(I.q, I.k, wl.block, wl.w_sink, wl.w_local, synth.TAU, synth.ALPHA, synth.GAMMA,
+                                I.bias_offsets, I.bias_values,
+                                keep_all=select_mode == crisp.SELECT_KEEP_ALL)
+    _cache[key] = (wl, I, X, spec, bufs, ref)
+    return _cache[key]
+
+
+def _check_attention(wl, I, X, spec, bufs, ref, rows, what, heads=None):
+    """Sparse and dense GPU outputs against the fp64 oracle at the given rows / heads."""
+    import torch
+    specs = oracle.specs_from_index_sets(ref)
+    hs = list(range(len(specs))) if heads is None else list(heads)
+    hsel = torch.as_tensor(hs, device="cuda")
+    with Timer(f"gpu sparse {what}"):
+        o_sp = rows_of(run_sparse(spec, X, bufs)[hsel], rows)
+    with Timer(f"oracle sparse {what}"):
+        r_sp = oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, bias_offsets=I.bias_offsets,
+                                bias_values=I.bias_values, heads=hs, chunk=512)
+    err_sp = np.abs(o_sp - r_sp).max()
+    with Timer(f"gpu dense {what}"):
+        o_de = rows_of(run_dense(spec, X)[hsel], rows)
+    with Timer(f"oracle dense {what}"):
+        r_de = oracle.attention(I.q, I.k, I.v, wl.block, [dict(kind="dense")] * len(specs), rows=rows,
+                                bias_offsets=I.bias_offsets, bias_values=I.bias_values, heads=hs, chunk=512)
+    err_de = np.abs(o_de - r_de).max()
+    log(what, "max-abs sparse", err_sp, "dense", err_de)
+    assert np.isfinite(o_sp).all() and np.isfinite(o_de).all()
+    assert err_sp <= TOL[wl.dtype], f"sparse max-abs {err_sp}"
+    assert err_de <= TOL[wl.dtype], f"dense max-abs {err_de}"
+
+
+ALL = ["tiny", "llama_32k", "llama_128k", "qwen_128k", "llama_512k"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ALL)
+def test_index_sets_bit_exact(name):
+    wl, I, X, spec, bufs, ref = _case(name)
+    gpu = download_index_sets(bufs)
+    bad = compare_index_sets(gpu, ref)
+    assert not bad, "\n".join(bad[:20])
+    # the planted heads route to VS, the i.i.d. heads to pooled estimation
+    expect = [1 if h in wl.planted_heads else 0 for h in range(wl.hq)]
+    assert gpu["route"].tolist() == expect
+    if name == "tiny":
+        _check_attention(wl, I, X, spec, bufs, ref, None, f"{name} all rows")
+    else:
+        _check_attention(wl, I, X, spec, bufs, ref, synth.sample_rows(wl), f"{name} 256 sampled rows")
+    if name == "llama_32k":
+        # every row of two VS and two PE heads (both kinds of KV group)
+        _check_attention(wl, I, X, spec, bufs, ref, None, f"{name} all rows, heads 0 1 16 17",
+                         heads=[0, 1, 16, 17])
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny", "llama_32k"])
+def test_keep_all_equals_dense(name):
+    """With every block kept, the sparse path is dense causal attention, bit for bit."""
+    wl, I, X, spec, bufs, ref = _case(name, select_mode=crisp.SELECT_KEEP_ALL)
+    gpu = download_index_sets(bufs)
+    bad = compare_index_sets(gpu, ref)
+    assert not bad, "\n".join(bad[:20])
+    o_sp = run_sparse(spec, X, bufs)
+    o_de = run_dense(spec, X)
+    import torch
+    assert torch.equal(o_sp, o_de)
+
+
+@pytest.mark.timeout(600)
+def test_determinism():
+    wl, I, X, spec, bufs, ref = _case("llama_32k")
+    import torch
+    o1 = run_sparse(spec, X, bufs)
+    b2 = run_route_select(spec, X)
+    for name in ("route", "cstruct_num", "mass_v", "mass_s", "mass_total", "vs_count", "vs_vertical", "vs_slash",
+                 "pe_rowptr"):
+        assert torch.equal(getattr(bufs, name), getattr(b2, name)), name
+    nnz = int(bufs.pe_rowptr[:, -1].max())
+    assert torch.equal(bufs.pe_col[:, :nnz], b2.pe_col[:, :nnz])
+    o2 = run_sparse(spec, X, b2)
+    assert torch.equal(o1, o2)
+    assert torch.equal(run_dense(spec, X), run_dense(spec, X))
+
+
+EDGE = {
+    "ragged_f32": synth.Workload(name="ragged_f32", hq=4, hkv=2, d=64, n=1000, dtype="f32", block=64,
+                                 rope_theta=0.0, seed=31, planted_heads=[0, 1], n_vertical=4,
+                                 vertical_gain=(3.0, 3.0), fixed_slash=(0, 5)),
+    "ragged_bf16": synth.Workload(name="ragged_bf16", hq=4, hkv=1, d=128, n=5000, dtype="bf16", block=128,
+                                  rope_theta=5e5, seed=32, planted_heads=[0], n_vertical=8),
+    "two_blocks_f32_d128": synth.Workload(name="two_blocks", hq=2, hkv=1, d=128, n=200, dtype="f32", block=128,
+                                          rope_theta=0.0, seed=33, planted_heads=[0], n_vertical=0,
+                                          fixed_slash=(0,)),
+    "one_block_bf16": synth.Workload(name="one_block", hq=2, hkv=2, d=128, n=100, dtype="bf16", block=128,
+                                     rope_theta=0.0, seed=34, planted_heads=[1], n_vertical=0, fixed_slash=(3,)),
+    "single_token": synth.Workload(name="single_token", hq=1, hkv=1, d=64, n=1, dtype="f32", block=64,
+                                   rope_theta=0.0, seed=35, planted_heads=[], n_vertical=0),
+    "bf16_b64_d64": synth.Workload(name="bf16_b64_d64", hq=4, hkv=2, d=64, n=3000, dtype="bf16", block=64,
+                                   rope_theta=1e4, seed=36, planted_heads=[0, 2], n_vertical=6),
+    "batch2_bf16": synth.Workload(name="batch2", hq=4, hkv=2, d=128, n=2100, dtype="bf16", block=128,
+                                  rope_theta=5e5, seed=37, planted_heads=[0, 1], n_vertical=5, batch=2),
+    "f32_b128_d128": synth.Workload(name="f32_b128_d128", hq=2, hkv=1, d=128, n=1500, dtype="f32", block=128,
+                                    rope_theta=0.0, seed=38, planted_heads=[0], n_vertical=3),
+}
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", list(EDGE))
+@pytest.mark.parametrize("mode", [crisp.SELECT_NOISE_FLOOR, crisp.SELECT_KEEP_ALL])
+def test_edge_shapes(name, mode):
+    wl, I, X, spec, bufs, ref = _case("edge_" + name, EDGE[name], mode)
+    gpu = download_index_sets(bufs)
+    bad = compare_index_sets(gpu, ref)
+    assert not bad, "\n".join(bad[:20])
+    _check_attention(wl, I, X, spec, bufs, ref, None, f"{name} mode {mode}")
+    if mode == crisp.SELECT_KEEP_ALL:
+        import torch
+        assert torch.equal(run_sparse(spec, X, bufs), run_dense(spec, X))
