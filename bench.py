@@ -1,0 +1,299 @@
+"""Benchmark: CRISP sparse-prefill attention per layer on one MI355X.
+
+One step = one pass of the whole sparse path on a layer resident in HBM:
+crisp_route (proxy map, C_struct routing) + crisp_select_indices (VS noise
+floor / PE index) + crisp_sparse_prefill (attention over the selected blocks).
+The library's own dense prefill (same tile engine) is timed beside it for the
+speedup.  Default workload: Llama-3.1-8B-shaped layer at n = 524288 (32 query
+/ 8 KV heads, d = 128, bf16, causal, synthetic planted inputs).
+
+Prints ONE JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "dynamic_sparse_attention_proxy_amd", "csrc", "attention.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(path=ATTN_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def tile_counts(bufs, spec):
+    """Computed 128x128 tiles per head of the sparse attention (host, from the index sets)."""
+    import numpy as np
+    nb = spec.num_blocks
+    route = bufs.route.cpu().numpy()
+    cnt = bufs.vs_count.cpu().numpy()
+    vv = bufs.vs_vertical.cpu().numpy()
+    ss = bufs.vs_slash.cpu().numpy()
+    rp = bufs.pe_rowptr.cpu().numpy()
+    qb = np.arange(nb)[:, None]
+    kb = np.arange(nb)[None, :]
+    delta = qb - kb
+    causal = delta >= 0
+    out = []
+    for h in range(len(route)):
+        if route[h]:
+            inv = np.zeros(nb + 1, bool)
+            inv[vv[h, : cnt[h, 0]]] = True
+            ins = np.zeros(nb + 2, bool)
+            ins[ss[h, : cnt[h, 1]]] = True
+            sel = causal & (inv[np.minimum(kb, nb)] | ins[np.clip(delta, 0, nb)] |
+                            ((delta >= 1) & ins[np.clip(delta - 1, 0, nb)]))
+            out.append(int(sel.sum()))
+        else:
+            out.append(int(rp[h, -1]))
+    return out
+
+
+def time_calls(fn, reps, stream):
+    import torch
+    start = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    end = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        start[i].record(stream)
+        fn()
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(start, end)]
+
+
+def cpu_baseline(wl, I, seconds_hint=20.0):
+    """The CPU oracle, timed on a bounded sample of the same layer and scaled to ms per layer."""
+    import numpy as np
+    import torch
+
+    import oracle
+    G = wl.hq // wl.hkv
+    nb = (wl.n + wl.block - 1) // wl.block
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # (1) routing: proxy map of the last block for two heads (one VS, one PE), scaled to all heads
+    heads = [wl.planted_heads[0], [h for h in range(wl.hq) if h not in wl.planted_heads][0]]
+    t = time.perf_counter()
+    pr = oracle.proxy(I.q[heads], I.k[[h // G for h in heads]], wl.block, wl.w_sink, wl.w_local, (1, 10),
+                      I.bias_offsets[heads], I.bias_values[heads])
+    t_route = (time.perf_counter() - t) / len(heads) * wl.hq
+    # (2) selection: VS lists for the VS head, the PE index for one PE head, scaled per route
+    t = time.perf_counter()
+    spec_vs = dict(kind="vs", vertical=oracle.vs_select(pr["mass_v"][0], pr["total"][0]),
+                   slash=oracle.vs_select(pr["mass_s"][0], pr["total"][0]))
+    t_vs = time.perf_counter() - t
+    t = time.perf_counter()
+    rowptr, cols = oracle.pe_index(I.q[heads[1]], I.k[heads[1] // G], wl.block, (19, 20))
+    t_pe = time.perf_counter() - t
+    n_vs = len(wl.planted_heads)
+    t_select = t_vs * n_vs + t_pe * (wl.hq - n_vs)
+    # (3) attention: 32 uniformly drawn rows of each of the two heads, scaled to all rows and heads
+    rng = np.random.default_rng(wl.seed + 1)
+    rows = np.sort(rng.choice(wl.n, size=32, replace=False))
+    specs = [None] * wl.hq
+    specs[heads[0]] = spec_vs
+    specs[heads[1]] = dict(kind="pe", rowptr=rowptr, cols=cols)
+    t = time.perf_counter()
+    oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, bias_offsets=I.bias_offsets,
+                     bias_values=I.bias_values, heads=[heads[0]], chunk=64)
+    t_att_vs = (time.perf_counter() - t) / len(rows) * wl.n
+    t = time.perf_counter()
+    oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, heads=[heads[1]], chunk=64)
+    t_att_pe = (time.perf_counter() - t) / len(rows) * wl.n
+    t_att = t_att_vs * n_vs + t_att_pe * (wl.hq - n_vs)
+    total_ms = (t_route + t_select + t_att) * 1e3
+    return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": max(threads, torch.get_num_threads()),
+            "kind": "oracle",
+            "sample": (f"oracle timed on heads {heads} (one VS, one PE): full proxy routing of both, VS selection, "
+                       f"the full PE index of one head, and masked fp64 attention on 32 uniform rows of each; "
+                       f"scaled to {wl.hq} heads and {wl.n} rows (extrapolated full-layer time)"),
+            "parts_ms": {"route": round(t_route * 1e3, 1), "select": round(t_select * 1e3, 1),
+                         "attention": round(t_att * 1e3, 1)}}
+
+
+def copy_calibration(gib: float = 4.0):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": 3}))
+
+
+def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
+    import torch
+
+    import dynamic_sparse_attention_proxy_amd as crisp
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    t = time.time()
+    I = synth.make_inputs(wl)
+    log(f"inputs {wl.name}: {time.time() - t:.1f}s")
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(I.q).cuda().to(dt)
+    k = torch.from_numpy(I.k).cuda().to(dt)
+    v = torch.from_numpy(I.v).cuda().to(dt)
+    bo = torch.from_numpy(I.bias_offsets).cuda()
+    bv = torch.from_numpy(I.bias_values).cuda()
+    spec = crisp.LayerSpec(batch=wl.batch, n_q_heads=wl.hq, n_kv_heads=wl.hkv, seq_len=wl.n, head_dim=wl.d,
+                           dtype=crisp.BF16 if wl.dtype == "bf16" else crisp.F32, block=wl.block,
+                           w_sink=wl.w_sink, w_local=wl.w_local, tau=synth.TAU, alpha=synth.ALPHA,
+                           gamma=synth.GAMMA)
+    bufs = crisp.Buffers(spec)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def route():
+        crisp.route(spec, q, k, bufs, bo, bv)
+
+    def select():
+        crisp.select_indices(spec, q, k, bufs)
+
+    def attend():
+        crisp.sparse_prefill(spec, q, k, v, o, bufs, bo, bv)
+
+    def step():
+        route()
+        select()
+        attend()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stage = {"route": [], "select": [], "attention": []}
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        route()
+        ev[i][1].record(stream)
+        select()
+        ev[i][2].record(stream)
+        attend()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(steps):
+        stage["route"].append(ev[i][0].elapsed_time(ev[i][1]))
+        stage["select"].append(ev[i][1].elapsed_time(ev[i][2]))
+        stage["attention"].append(ev[i][2].elapsed_time(ev[i][3]))
+    res = {"I": I, "spec": spec, "bufs": bufs, "wall_s": wall,
+           "stage_ms": {kk: sum(vv) / len(vv) for kk, vv in stage.items()}}
+    if with_dense:
+        od = torch.empty_like(q)
+        dense_reps = dense_reps or max(2, steps // 2)
+        crisp.dense_prefill(spec, q, k, v, od, bo, bv)
+        torch.cuda.synchronize()
+        res["dense_ms"] = sum(time_calls(lambda: crisp.dense_prefill(spec, q, k, v, od, bo, bv), dense_reps,
+                                         stream)) / dense_reps
+    res["tiles"] = tile_counts(bufs, spec)
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="llama_512k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-128k", action="store_true", help="skip the 128K speedup side measurement")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the CRISP path here is single-GPU (heads would shard across "
+              "GPUs with no communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import synth
+    wl = synth.WORKLOADS[args.config]
+    torch.cuda.set_device(0)
+    r = measure(wl, args.steps, args.warmup, with_dense=not args.no_dense)
+    st = r["stage_ms"]
+    total_ms = st["route"] + st["select"] + st["attention"]
+    tiles = sum(r["tiles"])
+    B, d = wl.block, wl.d
+    causal_tiles = wl.batch * wl.hq * ((wl.n + B - 1) // B) * ((wl.n + B - 1) // B + 1) // 2
+    flops = tiles * 4.0 * d * B * B
+    achieved = flops / (st["attention"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(args.config)
+        if ent and ent.get("source_sha") == source_hash():
+            traffic = ent.get("bytes_per_launch")
+    out = {
+        "metric": "sparse-prefill attention ms/layer + speedup vs own dense at 128K/512K, 1 GPU",
+        "value": round(total_ms, 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_s"] / args.steps * 1e3, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded planted VS heads + i.i.d. heads; random values, no weights)",
+        "config": {"workload": wl.description, "seq_len": wl.n, "q_heads": wl.hq, "kv_heads": wl.hkv,
+                   "head_dim": d, "block": B, "tau": "1/10", "alpha": "1/1", "gamma": "19/20"},
+        "tokens_per_s": round(wl.n / (total_ms * 1e-3), 1),
+        "stage_ms": {kk: round(vv, 3) for kk, vv in st.items()},
+        "tile_density": round(tiles / causal_tiles, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel (crisp_sparse_prefill launch)",
+                     "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": flops},
+        "context": {"pages_attention_speedup_512k": "up to 5.30x (real model maps; hardware not stated)"},
+    }
+    if "dense_ms" in r:
+        out["dense_ms_per_layer"] = round(r["dense_ms"], 3)
+        out["speedup_vs_dense"] = round(r["dense_ms"] / total_ms, 3)
+        out["speedup_attention_only"] = round(r["dense_ms"] / st["attention"], 3)
+        dense_flops = wl.batch * wl.hq * 4.0 * d * wl.n * (wl.n + 1) / 2
+        out["dense_tflops_useful"] = round(dense_flops / (r["dense_ms"] * 1e-3) / 1e12, 1)
+    if not args.no_128k and args.config == "llama_512k" and not args.no_dense:
+        r2 = measure(synth.WORKLOADS["llama_128k"], 3, 1)
+        st2 = r2["stage_ms"]
+        tot2 = st2["route"] + st2["select"] + st2["attention"]
+        out["at_128k"] = {"sparse_ms_per_layer": round(tot2, 3), "dense_ms_per_layer": round(r2["dense_ms"], 3),
+                          "speedup_vs_dense": round(r2["dense_ms"] / tot2, 3),
+                          "stage_ms": {kk: round(vv, 3) for kk, vv in st2.items()}}
+        del r2
+    if not args.no_cpu_baseline:
+        t = time.time()
+        out["cpu_baseline"] = cpu_baseline(wl, r["I"])
+        log(f"cpu baseline {time.time() - t:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,7 @@ struct Layout {
   // select
   size_t s_qbar, s_kbar, s_zbar, s_abar, s_rowtot, s_hist, s_state, s_gt, s_tie, s_tiep, s_end;
   // sparse attention
-  size_t a_tiles, a_cnt, a_end;
+  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_end;
   size_t total;
 };
 
@@ -103,6 +103,11 @@ Layout layout(const Dims& d) {
   o = align_up(o + (size_t)d.bh * d.ntri * sizeof(int));
   L.a_cnt = o;
   o = align_up(o + (size_t)d.bh * d.nb * sizeof(int));
+  const size_t pairs = (size_t)d.bkv * ((d.group + 1) / 2);
+  L.a_ulist = o;
+  o = align_up(o + pairs * d.ntri * sizeof(int));
+  L.a_ucnt = o;
+  o = align_up(o + pairs * d.nb * sizeof(int));
   L.a_end = o;
 
   L.total = L.r_end;
@@ -278,10 +283,12 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
   char* w = static_cast<char*>(ws);
   int* tiles = reinterpret_cast<int*>(w + L.a_tiles);
   int* cnt = reinterpret_cast<int*>(w + L.a_cnt);
+  int* ulist = reinterpret_cast<int*>(w + L.a_ulist);
+  int* ucnt = reinterpret_cast<int*>(w + L.a_ucnt);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (launch_build_tiles(d, index_out(idx), tiles, cnt, st) != hipSuccess) return CRISP_ERR_HIP;
-  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, st) != hipSuccess) return CRISP_ERR_HIP;
+  if (launch_build_tiles(d, index_out(idx), tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
+  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
   return hip_status();
 }
 
@@ -297,7 +304,8 @@ crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* c
   BiasArgs ba;
   CRISP_TRY(check_bias(bias, &ba));
   (void)hipGetLastError();
-  if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }

@@ -74,10 +74,14 @@ hipError_t launch_route(const Dims& dm, const RouteArgs& ra, const BiasArgs& bia
 hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, const void* k,
                          const SelectScratch& ws, const IndexOut& io, hipStream_t st);
 // attention.hip
-hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt,
-                              hipStream_t st);
+bool use_matrix_engine(const Dims& dm);  // bf16, d = 128, B = 128
+// per-head tile lists [bh][ntri] + counts [bh][nb]; for the matrix engine also the
+// union lists of query-head pairs [bkv * pairs][ntri] + counts [bkv * pairs][nb]
+hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt, int* ulist,
+                              int* ucnt, hipStream_t st);
+// tiles == nullptr: dense causal
 hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q, const void* k,
-                            const void* v, void* o, const int* tiles, const int* tile_cnt,
-                            hipStream_t st);
+                            const void* v, void* o, const int* tiles, const int* tile_cnt, const int* ulist,
+                            const int* ucnt, hipStream_t st);
 
 }  // namespace crisp
