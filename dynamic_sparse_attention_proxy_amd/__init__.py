@@ -56,9 +56,11 @@ class CrispError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libcrisp.so (built by ``dynamic_sparse_attention_proxy_amd.build``); raise if missing."""
+def load_library(path: str = None):
+    """Load libcrisp.so (built by ``dynamic_sparse_attention_proxy_amd.build``, or the
+    build named by the CRISP_LIB environment variable); raise if missing."""
     global _lib
+    path = path or os.environ.get("CRISP_LIB") or LIB_PATH
     if _lib is None:
         if not os.path.exists(path):
             raise CrispError(f"{path} is missing: build it with `python -m dynamic_sparse_attention_proxy_amd.build`")

@@ -95,12 +95,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  // round to nearest even (finite inputs)
-  unsigned a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a = (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
-  b = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
-  return a | b;
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
+}
+
+// sum of a packed bf16 pair added to acc (v_dot2 with (1, 1))
+__device__ __forceinline__ float sum_bf16x2(unsigned pr, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), one, acc, false);
 }
 
 // key row inside a 32-key group that feeds matrix row rho (swap of bits 2 and 3)
@@ -113,11 +120,14 @@ __device__ __forceinline__ int key_perm(int rho) {
 // the pairs of one KV head are 8 items apart so they land on the same XCD
 // (shared K/V in its L2), and the KV head served by an XCD rotates with the
 // level so that cheap (VS) and expensive (PE) groups alternate on every XCD.
+#ifndef CRISP_ROT_PERIOD
+#define CRISP_ROT_PERIOD 1
+#endif
 __device__ __forceinline__ void pair_item(const Dims& dm, int pairs, int L, int* qb, int* g, int* w) {
   const int U = dm.bkv * pairs;
   const int level = L / U, p = L % U;
   *w = p / dm.bkv;
-  *g = (p % dm.bkv + level) % dm.bkv;
+  *g = (p % dm.bkv + level / CRISP_ROT_PERIOD) % dm.bkv;
   *qb = dm.nb - 1 - level;
 }
 
@@ -234,6 +244,7 @@ __global__ __launch_bounds__(512 / QG, 1) void attn_mfma_kernel(const bf16_t* __
     }
   };
   auto store_v = [&](bf16_t* Vt, const uint4* src) {
+    // 8 keys x 8 dims -> 8 dims x 8 keys: dword w of key row e holds dims (2w, 2w+1)
 #pragma unroll
     for (int wd = 0; wd < 4; ++wd) {
       unsigned lo[4], hi[4];
@@ -242,8 +253,8 @@ __global__ __launch_bounds__(512 / QG, 1) void attn_mfma_kernel(const bf16_t* __
         const uint4 a0 = src[2 * pp], a1 = src[2 * pp + 1];
         const unsigned ev = wd == 0 ? a0.x : wd == 1 ? a0.y : wd == 2 ? a0.z : a0.w;
         const unsigned od = wd == 0 ? a1.x : wd == 1 ? a1.y : wd == 2 ? a1.z : a1.w;
-        lo[pp] = (ev & 0xffffu) | (od << 16);
-        hi[pp] = (ev >> 16) | (od & 0xffff0000u);
+        lo[pp] = __builtin_amdgcn_perm(od, ev, 0x05040100u);  // low halves: dim 2w of keys 2pp, 2pp+1
+        hi[pp] = __builtin_amdgcn_perm(od, ev, 0x07060302u);  // high halves: dim 2w+1
       }
       const int r0 = dg * 8 + 2 * wd;
       *reinterpret_cast<uint4*>(Vt + v_off(r0) + kg * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
@@ -307,51 +318,55 @@ __global__ __launch_bounds__(512 / QG, 1) void attn_mfma_kernel(const bf16_t* __
               sacc[qg][a2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qreg[qg][kc], sacc[qg][a2], 0, 0, 0);
           }
         }
+        const bool slow = masked || tile_bias;
+        unsigned pk2[QG][2][8];  // probabilities as packed bf16 pairs, per (a2, x / 2)
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) {
           // element (a2, x) of this lane is key column c = C + 8 hl of the tile with the
           // compile-time C = 32 (2 kh + a2) + 16 (x >> 3) + (x & 7); its query row is r
-#pragma unroll
-          for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) sacc[qg][a2][x] *= sl2;
-          int rr = r_in_blk[qg] - 8 * hl;  // r >= c  <=>  rr >= C
-          // keep the per-element compares inside the loop (hoisting them costs 256 SGPRs)
-          asm volatile("" : "+v"(rr));
-          if (tile_bias) {
-            for (int t2 = 0; t2 < bias.count; ++t2) {
-              const int off = bias.offsets[(size_t)bh * bias.count + t2];
-              const float bv = bias.values[(size_t)bh * bias.count + t2] * log2e;
-              const int cstar = rr - (off - (qb - kb) * B);  // r - c == off  <=>  C == cstar
-#pragma unroll
-              for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-                for (int x = 0; x < 16; ++x)
-                  if (32 * (2 * kh + a2) + 16 * (x >> 3) + (x & 7) == cstar) sacc[qg][a2][x] += bv;
-            }
-          }
-          if (masked) {
-            const bool lower_ok = (mode & kModeLower) != 0;
-            const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
-            const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
+          if (slow) {
 #pragma unroll
             for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-              for (int x = 0; x < 16; ++x) {
-                const int C = 32 * (2 * kh + a2) + 16 * (x >> 3) + (x & 7);
-                const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
-                if (!keep) sacc[qg][a2][x] = -__builtin_inff();
+              for (int x = 0; x < 16; ++x) sacc[qg][a2][x] *= sl2;
+            int rr = r_in_blk[qg] - 8 * hl;  // r >= c  <=>  rr >= C
+            // keep the per-element compares inside the loop (hoisting them costs 256 SGPRs)
+            asm volatile("" : "+v"(rr));
+            if (tile_bias) {
+              for (int t2 = 0; t2 < bias.count; ++t2) {
+                const int off = bias.offsets[(size_t)bh * bias.count + t2];
+                const float bv = bias.values[(size_t)bh * bias.count + t2] * log2e;
+                const int cstar = rr - (off - (qb - kb) * B);  // r - c == off  <=>  C == cstar
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                  for (int x = 0; x < 16; ++x)
+                    if (32 * (2 * kh + a2) + 16 * (x >> 3) + (x & 7) == cstar) sacc[qg][a2][x] += bv;
               }
+            }
+            if (masked) {
+              const bool lower_ok = (mode & kModeLower) != 0;
+              const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
+              const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
+#pragma unroll
+              for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                  const int C = 32 * (2 * kh + a2) + 16 * (x >> 3) + (x & 7);
+                  const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
+                  if (!keep) sacc[qg][a2][x] = -__builtin_inff();
+                }
+            }
           }
+          // row max of this half (raw scores on the fast path: the scale is positive)
           float mx = -__builtin_inff();
 #pragma unroll
           for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) mx = sacc[qg][a2][x] > mx ? sacc[qg][a2][x] : mx;
-          {
-            const float ot = __shfl_xor(mx, 32);
-            mx = ot > mx ? ot : mx;
-          }
+            for (int x = 0; x < 16; x += 2) mx = fmaxf(mx, fmaxf(sacc[qg][a2][x], sacc[qg][a2][x + 1]));
+          const float ksc = slow ? 1.0f : sl2;  // multiplier from stored scores to log2 units
+          mx *= ksc;
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
           // lazy rescaling: the running max moves (and O, l are rescaled) only when
           // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
           if (__any(mx > m_run[qg] + 8.0f)) {
@@ -366,16 +381,17 @@ __global__ __launch_bounds__(512 / QG, 1) void attn_mfma_kernel(const bf16_t* __
               for (int x = 0; x < 16; ++x) oacc[qg][t2][x] *= alpha;
           }
           const float m_use = m_run[qg] == -__builtin_inff() ? 0.0f : m_run[qg];
-          float psum = 0.0f;
+          float psum = l_run[qg];
 #pragma unroll
           for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-              const float p = __builtin_amdgcn_exp2f(sacc[qg][a2][x] - m_use);
-              sacc[qg][a2][x] = p;
-              psum += p;
+            for (int x = 0; x < 16; x += 2) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qg][a2][x], ksc, -m_use));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qg][a2][x + 1], ksc, -m_use));
+              pk2[qg][a2][x >> 1] = pack_bf16x2(p0, p1);
+              psum = sum_bf16x2(pk2[qg][a2][x >> 1], psum);
             }
-          l_run[qg] += psum;
+          l_run[qg] = psum;
         }
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2) {
@@ -383,14 +399,9 @@ __global__ __launch_bounds__(512 / QG, 1) void attn_mfma_kernel(const bf16_t* __
           for (int s2 = 0; s2 < 2; ++s2) {
             bf16x8_t P[QG];
 #pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-              uint4 pu;
-              pu.x = pack_bf16x2(sacc[qg][a2][8 * s2 + 0], sacc[qg][a2][8 * s2 + 1]);
-              pu.y = pack_bf16x2(sacc[qg][a2][8 * s2 + 2], sacc[qg][a2][8 * s2 + 3]);
-              pu.z = pack_bf16x2(sacc[qg][a2][8 * s2 + 4], sacc[qg][a2][8 * s2 + 5]);
-              pu.w = pack_bf16x2(sacc[qg][a2][8 * s2 + 6], sacc[qg][a2][8 * s2 + 7]);
-              P[qg] = as_bf16x8(pu);
-            }
+            for (int qg = 0; qg < QG; ++qg)
+              P[qg] = as_bf16x8(make_uint4(pk2[qg][a2][4 * s2 + 0], pk2[qg][a2][4 * s2 + 1], pk2[qg][a2][4 * s2 + 2],
+                                           pk2[qg][a2][4 * s2 + 3]));
             const int a = 2 * kh + a2;
 #pragma unroll
             for (int t2 = 0; t2 < 4; ++t2) {
