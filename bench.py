@@ -101,26 +101,32 @@ def cpu_baseline(wl, I, seconds_hint=20.0):
     t_pe = time.perf_counter() - t
     n_vs = len(wl.planted_heads)
     t_select = t_vs * n_vs + t_pe * (wl.hq - n_vs)
-    # (3) attention: 32 uniformly drawn rows of each of the two heads, scaled to all rows and heads
+    # (3) attention: the marginal cost per row (two sample sizes of uniformly drawn rows)
+    #     plus the fixed per-head cost, scaled to every row of every head
     rng = np.random.default_rng(wl.seed + 1)
-    rows = np.sort(rng.choice(wl.n, size=32, replace=False))
     specs = [None] * wl.hq
     specs[heads[0]] = spec_vs
     specs[heads[1]] = dict(kind="pe", rowptr=rowptr, cols=cols)
-    t = time.perf_counter()
-    oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, bias_offsets=I.bias_offsets,
-                     bias_values=I.bias_values, heads=[heads[0]], chunk=64)
-    t_att_vs = (time.perf_counter() - t) / len(rows) * wl.n
-    t = time.perf_counter()
-    oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, heads=[heads[1]], chunk=64)
-    t_att_pe = (time.perf_counter() - t) / len(rows) * wl.n
-    t_att = t_att_vs * n_vs + t_att_pe * (wl.hq - n_vs)
+    per_head = []
+    for h in heads:
+        times = []
+        for nrows in (32, 96):
+            rows = np.sort(rng.choice(wl.n, size=nrows, replace=False))
+            t = time.perf_counter()
+            oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, bias_offsets=I.bias_offsets,
+                             bias_values=I.bias_values, heads=[h], chunk=64)
+            times.append(time.perf_counter() - t)
+        marginal = max(times[1] - times[0], 0.0) / 64
+        fixed = max(times[0] - 32 * marginal, 0.0)
+        per_head.append(fixed + marginal * wl.n)
+    t_att = per_head[0] * n_vs + per_head[1] * (wl.hq - n_vs)
     total_ms = (t_route + t_select + t_att) * 1e3
     return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": max(threads, torch.get_num_threads()),
             "kind": "oracle",
             "sample": (f"oracle timed on heads {heads} (one VS, one PE): full proxy routing of both, VS selection, "
-                       f"the full PE index of one head, and masked fp64 attention on 32 uniform rows of each; "
-                       f"scaled to {wl.hq} heads and {wl.n} rows (extrapolated full-layer time)"),
+                       f"the full PE index of one head, and masked fp64 attention on 32 and 96 uniform rows of "
+                       f"each (marginal cost per row + fixed cost per head); scaled to {wl.hq} heads and "
+                       f"{wl.n} rows (extrapolated full-layer time)"),
             "parts_ms": {"route": round(t_route * 1e3, 1), "select": round(t_select * 1e3, 1),
                          "attention": round(t_att * 1e3, 1)}}
 

@@ -15,6 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "crisp")
 LIB = os.path.join(HERE, "libcrisp.so")
 SOURCES = ["route.hip", "select.hip", "attention.hip", "abi.hip"]
+EXTRA = {}  # per-source extra flags
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -29,7 +30,7 @@ FLAGS = [
 
 def _compile(src: str, obj_dir: str = OBJ, defines=()) -> str:
     out = os.path.join(obj_dir, src + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

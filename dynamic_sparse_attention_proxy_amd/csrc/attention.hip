@@ -120,14 +120,11 @@ __device__ __forceinline__ int key_perm(int rho) {
 // the pairs of one KV head are 8 items apart so they land on the same XCD
 // (shared K/V in its L2), and the KV head served by an XCD rotates with the
 // level so that cheap (VS) and expensive (PE) groups alternate on every XCD.
-#ifndef CRISP_ROT_PERIOD
-#define CRISP_ROT_PERIOD 1
-#endif
 __device__ __forceinline__ void pair_item(const Dims& dm, int pairs, int L, int* qb, int* g, int* w) {
   const int U = dm.bkv * pairs;
   const int level = L / U, p = L % U;
   *w = p / dm.bkv;
-  *g = (p % dm.bkv + level / CRISP_ROT_PERIOD) % dm.bkv;
+  *g = (p % dm.bkv + level) % dm.bkv;
   *qb = dm.nb - 1 - level;
 }
 
