@@ -208,9 +208,9 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
     if with_dense:
         od = torch.empty_like(q)
         dense_reps = dense_reps or max(2, steps // 2)
-        crisp.dense_prefill(spec, q, k, v, od, bo, bv)
+        crisp.dense_prefill(spec, q, k, v, od, bufs, bo, bv)
         torch.cuda.synchronize()
-        res["dense_ms"] = sum(time_calls(lambda: crisp.dense_prefill(spec, q, k, v, od, bo, bv), dense_reps,
+        res["dense_ms"] = sum(time_calls(lambda: crisp.dense_prefill(spec, q, k, v, od, bufs, bo, bv), dense_reps,
                                          stream)) / dense_reps
     res["tiles"] = tile_counts(bufs, spec)
     del q, k, v, o

@@ -78,7 +78,7 @@ def load_library(path: str = None):
         lib.crisp_sparse_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), ctypes.POINTER(IndexSets), P,
                                              ctypes.c_size_t, P, P]
         lib.crisp_sparse_prefill.restype = ctypes.c_int
-        lib.crisp_dense_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), P, P]
+        lib.crisp_dense_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), P, ctypes.c_size_t, P, P]
         lib.crisp_dense_prefill.restype = ctypes.c_int
         lib.crisp_status_string.argtypes = [ctypes.c_int]
         lib.crisp_status_string.restype = ctypes.c_char_p
@@ -206,12 +206,14 @@ def sparse_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None
                                                _stream(stream)), "crisp_sparse_prefill")
 
 
-def dense_prefill(spec: LayerSpec, q, k, v, o, bias_offsets=None, bias_values=None, stream=None):
-    """crisp_dense_prefill: full causal attention with the same tile engine."""
+def dense_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None,
+                  stream=None):
+    """crisp_dense_prefill: full causal attention with the same tile engine (``bufs`` supplies the workspace)."""
     b = _bias(bias_offsets, bias_values)
     _check(load_library().crisp_dense_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
                                               q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(b),
-                                              o.data_ptr(), _stream(stream)), "crisp_dense_prefill")
+                                              bufs.ws.data_ptr(), bufs.ws_bytes, o.data_ptr(), _stream(stream)),
+           "crisp_dense_prefill")
 
 
 def prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):

@@ -24,8 +24,8 @@ struct Layout {
   size_t r_S, r_m, r_L, r_part, r_end;
   // select
   size_t s_qbar, s_kbar, s_zbar, s_abar, s_rowtot, s_hist, s_state, s_gt, s_tie, s_tiep, s_end;
-  // sparse attention
-  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_end;
+  // attention
+  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_vt, a_end;
   size_t total;
 };
 
@@ -108,6 +108,8 @@ Layout layout(const Dims& d) {
   o = align_up(o + pairs * d.ntri * sizeof(int));
   L.a_ucnt = o;
   o = align_up(o + pairs * d.nb * sizeof(int));
+  L.a_vt = o;
+  if (use_matrix_engine(d)) o = align_up(o + (size_t)d.bkv * d.d * d.nb * d.B * 2);  // V^T, bf16
   L.a_end = o;
 
   L.total = L.r_end;
@@ -288,24 +290,29 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (launch_build_tiles(d, index_out(idx), tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
-  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
+  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, w + L.a_vt, st) != hipSuccess)
+    return CRISP_ERR_HIP;
   return hip_status();
 }
 
 crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
-                                 const void* k, const void* v, const crisp_rel_bias* bias, void* o,
-                                 void* stream) {
+                                 const void* k, const void* v, const crisp_rel_bias* bias, void* ws,
+                                 size_t ws_bytes, void* o, void* stream) {
   Dims d;
   CRISP_TRY(make_dims(shape, cfg, &d));
   CRISP_TRY(check_tensor(q));
   CRISP_TRY(check_tensor(k));
   CRISP_TRY(check_tensor(v));
   CRISP_TRY(check_tensor(o));
+  CRISP_TRY(check_tensor(ws));
   BiasArgs ba;
   CRISP_TRY(check_bias(bias, &ba));
+  const Layout L = layout(d);
+  if (ws_bytes < L.total) return CRISP_ERR_WORKSPACE;
+  char* w = static_cast<char*>(ws);
   (void)hipGetLastError();
-  if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
+  if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, nullptr, nullptr, w + L.a_vt,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }

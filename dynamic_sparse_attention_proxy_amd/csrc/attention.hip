@@ -26,10 +26,6 @@ namespace crisp {
 
 namespace {
 
-#ifndef CRISP_ATTN_QG
-#define CRISP_ATTN_QG 1
-#endif
-
 constexpr int kModeLower = 1;  // r >= c inside the tile
 constexpr int kModeUpper = 2;  // r <  c inside the tile
 constexpr int kModeFull = 3;
@@ -92,11 +88,12 @@ __device__ __forceinline__ bool tile_keep(int mode, bool diag, int r, int c) {
 // ------------------------------------------------------- matrix engine ----
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
@@ -115,6 +112,34 @@ __device__ __forceinline__ int key_perm(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds_base + 16 i.  Written as inline assembly so that the compiler does
+// not treat the asynchronous LDS write as aliasing the LDS reads of the tile
+// being computed (it would wait for the prefetch before every read); the
+// kernel itself waits for completion (vmcnt) and synchronises (s_barrier)
+// before a tile is read.  base and lds_base are uniform over the wave.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+// the same with a per-lane 64-bit address
+__device__ __forceinline__ void dma16_lane(const unsigned char* addr, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(addr), "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+
+// keeps a value materialised at this point (no sinking past later branches)
+__device__ __forceinline__ void pin(unsigned x) { asm volatile("" ::"v"(x)); }
+
+__device__ __forceinline__ uint4 lds_read16(const unsigned char* p) { return *reinterpret_cast<const uint4*>(p); }
+
 // Work item of the matrix engine: (KV head g, pair w of its query heads, query
 // block qb).  Items are ordered by query block, heaviest first; inside a level
 // the pairs of one KV head are 8 items apart so they land on the same XCD
@@ -128,315 +153,300 @@ __device__ __forceinline__ void pair_item(const Dims& dm, int pairs, int L, int*
   *qb = dm.nb - 1 - level;
 }
 
-// LDS layout of one K / V^T tile pair.  Rows are padded to 272 bytes so that
-// every fragment address is a per-lane base plus a compile-time offset; V^T
-// rows get a further 16-byte skew per group of 8 rows so the transposing
-// stores of 16 lanes spread over the banks.
-constexpr int kRowK = 136;                                  // bf16 per K row (256 B + 16 B pad)
-constexpr int kTileK = 128 * kRowK;                         // 17408 bf16
-constexpr int kRowV = 136;
-__device__ __forceinline__ int v_off(int row) { return row * kRowV + (row >> 3) * 8; }
-constexpr int kTileV = 128 * kRowV + 16 * 8;                // 17536 bf16
-constexpr int kBuf = kTileK + kTileV;                       // one stage: 69888 bytes
+// LDS tiles are 128 rows of 256 bytes; the sixteen 16-byte chunks of a row are
+// stored XOR-swizzled so that the 16 lanes of a matrix-operand read (16
+// different rows, one chunk column) hit 16 different chunk positions:
+//   K tile   : row = key, chunk c (8 dims)    stored at c ^ key_perm(row & 15)
+//   V^T tile : row = dim, chunk c (8 keys)    stored at c ^ (row & 15)
+// Tiles are written by direct global-to-LDS loads: one wave instruction fills
+// 4 rows (1 KiB), lane i writing slot (i & 15) of row i >> 4, so the swizzle is
+// applied by choosing which global chunk each lane fetches.
+constexpr int kTileBytes = 128 * 256;
 
-// Matrix engine.  A workgroup serves 256 query rows that share every K/V tile:
-// the two query heads of a pair x the 128 rows of query block qb.  Each wave
-// owns QG groups of 32 query rows of one head (QG = 1: 8 waves, two per SIMD;
-// QG = 2: 4 waves, one per SIMD, every K or V fragment read from LDS feeding
-// two matrix instructions).  A 128-key tile is processed as two halves of 64
-// keys.  K and V of tile t + 2 are fetched into registers while tile t is
-// computed, and written to the other LDS stage before the barrier that ends
-// the iteration.
-template <bool kDense, int QG>
-__global__ __launch_bounds__(512 / QG, 1) void attn_mfma_kernel(const bf16_t* __restrict__ q,
-                                                                const bf16_t* __restrict__ k,
-                                                                const bf16_t* __restrict__ v,
-                                                                bf16_t* __restrict__ o, Dims dm, BiasArgs bias,
-                                                                const int* __restrict__ ulist,
-                                                                const int* __restrict__ ucnt, int pairs) {
+// Matrix engine.  A workgroup of 8 waves serves 256 query rows that share every
+// K/V tile: the two query heads of a pair x the 128 rows of query block qb;
+// wave w owns 32 rows of head w / 4 (two waves per SIMD).  A 128-key tile is
+// processed in four 32-key quarters: the softmax of quarter a runs on the
+// vector ALU while the matrix core computes the scores of quarter a + 1 and the
+// P V product of quarter a - 1.  Scores are computed transposed, S^T = K Q^T, so
+// a lane holds one query's scores; O^T = V^T P^T takes the probabilities
+// straight from registers.  K and V^T tiles are double-buffered in LDS: tile
+// t + 1 is in flight while tile t is computed.
+template <bool kDense>
+__global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restrict__ q,
+                                                           const bf16_t* __restrict__ k,
+                                                           const bf16_t* __restrict__ vt,
+                                                           bf16_t* __restrict__ o, Dims dm, BiasArgs bias,
+                                                           const int* __restrict__ ulist,
+                                                           const int* __restrict__ ucnt, int pairs, int npad) {
   constexpr int B = 128, D = 128;
-  constexpr int NT = 512 / QG;            // threads per workgroup
-  constexpr int WPH = 4 / QG;             // waves per head
-  constexpr int CH = (2 * 128 * 16) / NT; // 16-byte chunks of K (and of V) each thread stages
-  __shared__ __align__(16) bf16_t lds[2 * kBuf];
+  __shared__ __align__(1024) unsigned char sK0[kTileBytes];
+  __shared__ __align__(1024) unsigned char sK1[kTileBytes];
+  __shared__ __align__(1024) unsigned char sV0[kTileBytes];
+  __shared__ __align__(1024) unsigned char sV1[kTileBytes];
 
   int qb, g, w;
   pair_item(dm, pairs, blockIdx.x, &qb, &g, &w);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = wave / WPH, wr = wave % WPH;
-  const int hl = lane >> 5, ql = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave-level addresses scalar
+  const int slot = wave >> 2;
+  const int hl = lane >> 5, ql = lane & 31, l15 = lane & 15;
   const int bidx = g / dm.hkv, gh = g % dm.hkv;
   const int hin = 2 * w + slot;
   const bool slot_on = hin < dm.group;
   const int bh = bidx * dm.hq + gh * dm.group + (slot_on ? hin : 0);
   const bf16_t* qp = q + (size_t)bh * dm.n * D;
-  const bf16_t* kp = k + (size_t)g * dm.n * D;
-  const bf16_t* vp = v + (size_t)g * dm.n * D;
-  int r_in_blk[QG], qrow[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    r_in_blk[qg] = wr * 32 * QG + qg * 32 + ql;
-    qrow[qg] = qb * B + r_in_blk[qg];
-  }
+  const unsigned char* kp = reinterpret_cast<const unsigned char*>(k + (size_t)g * dm.n * D);
+  const unsigned char* vp = reinterpret_cast<const unsigned char*>(vt + (size_t)g * D * npad);
+  const int r_in_blk = (wave & 3) * 32 + ql;
+  const int qrow = qb * B + r_in_blk;
 
-  bf16x8_t qreg[QG][8];
+  bf16x8_t qreg[8];
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg)
+  for (int kc = 0; kc < 8; ++kc) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (slot_on && qrow < dm.n) u = *reinterpret_cast<const uint4*>(qp + (size_t)qrow * D + 16 * kc + 8 * hl);
+    qreg[kc] = as_bf16x8(u);
+  }
+  f32x16 oacc[4];
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (slot_on && qrow[qg] < dm.n)
-        u = *reinterpret_cast<const uint4*>(qp + (size_t)qrow[qg] * D + 16 * kc + 8 * hl);
-      qreg[qg][kc] = as_bf16x8(u);
-    }
-  f32x16 oacc[QG][4];
+  for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[qg][t][e] = 0.0f;
-  float m_run[QG], l_run[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) m_run[qg] = -__builtin_inff(), l_run[qg] = 0.0f;
+    for (int e = 0; e < 16; ++e) oacc[t2][e] = 0.0f;
+  float m_run = -__builtin_inff(), l_run = 0.0f;
   const float log2e = 1.4426950408889634f;
   const float sl2 = (float)(1.0 / __builtin_sqrt(128.0)) * log2e;
-  // per-lane fragment bases (elements); everything else is a constant offset
-  const int kfrag = key_perm(ql) * kRowK + 8 * hl;
-  const int vfrag = v_off(ql) + 8 * hl;
+
+  // per-lane byte offsets of the matrix operands inside a tile
+  int koff[8], voff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = key_perm(ql) * 256 + (((2 * kc + hl) ^ l15) << 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) voff[j] = ql * 256 + (((2 * j + hl) ^ l15) << 4);  // j = 2 a + s2
+  // per-lane source offsets of the direct loads: instruction i of the wave fills
+  // rows 4 m .. 4 m + 3 of a tile, m = 4 wave + i
+  unsigned dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * i + (lane >> 4);
+    dk[i] = (lane >> 4) * 256 + (((lane & 15) ^ key_perm(rr)) << 4);
+    dv[i] = (lane >> 4) * npad * 2 + (((lane & 15) ^ rr) << 4);
+  }
+
+  // this head's relative-position bias (at most 8 offsets), held in scalar registers
+  int boff[8];
+  float bval[8];
+#pragma unroll
+  for (int t2 = 0; t2 < 8; ++t2) {
+    boff[t2] = t2 < bias.count ? __builtin_amdgcn_readfirstlane(bias.offsets[(size_t)bh * bias.count + t2]) : -1;
+    bval[t2] = t2 < bias.count
+                   ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                         int, bias.values[(size_t)bh * bias.count + t2] * log2e)))
+                   : 0.0f;
+  }
 
   const int item = g * pairs + w;
   const int ntile = kDense ? qb + 1 : ucnt[(size_t)item * dm.nb + qb];
   const int* tl = kDense ? nullptr : ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
-
-  // staging.  QG = 2: every thread moves 8 chunks of K and an 8 x 8 block of V.
-  // QG = 1: threads 0..255 move K (8 chunks each), threads 256..511 the V blocks.
-  const int st = tid & 255;
-  const bool do_k = QG == 2 || tid < 256;
-  const bool do_v = QG == 2 || tid >= 256;
-  const int kg = st >> 4, dg = st & 15;
-  uint4 pk[QG == 2 ? 8 : 8], pv[QG == 2 ? 8 : 1];
-  (void)CH;
-  auto load_tile = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (QG == 2) {
-        const int id = st + 256 * i;
-        const int key = kb * B + (id >> 4);
-        pk[i] = make_uint4(0, 0, 0, 0);
-        if (key < dm.n) pk[i] = *reinterpret_cast<const uint4*>(kp + (size_t)key * D + (id & 15) * 8);
-        const int vkey = kb * B + kg * 8 + i;
-        pv[QG == 2 ? i : 0] = make_uint4(0, 0, 0, 0);
-        if (vkey < dm.n) pv[QG == 2 ? i : 0] = *reinterpret_cast<const uint4*>(vp + (size_t)vkey * D + dg * 8);
-      } else if (do_k) {
-        const int id = st + 256 * i;
-        const int key = kb * B + (id >> 4);
-        pk[i] = make_uint4(0, 0, 0, 0);
-        if (key < dm.n) pk[i] = *reinterpret_cast<const uint4*>(kp + (size_t)key * D + (id & 15) * 8);
-      } else {
-        const int vkey = kb * B + kg * 8 + i;
-        pk[i] = make_uint4(0, 0, 0, 0);
-        if (vkey < dm.n) pk[i] = *reinterpret_cast<const uint4*>(vp + (size_t)vkey * D + dg * 8);
-      }
-    }
-  };
-  auto store_v = [&](bf16_t* Vt, const uint4* src) {
-    // 8 keys x 8 dims -> 8 dims x 8 keys: dword w of key row e holds dims (2w, 2w+1)
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      unsigned lo[4], hi[4];
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const uint4 a0 = src[2 * pp], a1 = src[2 * pp + 1];
-        const unsigned ev = wd == 0 ? a0.x : wd == 1 ? a0.y : wd == 2 ? a0.z : a0.w;
-        const unsigned od = wd == 0 ? a1.x : wd == 1 ? a1.y : wd == 2 ? a1.z : a1.w;
-        lo[pp] = __builtin_amdgcn_perm(od, ev, 0x05040100u);  // low halves: dim 2w of keys 2pp, 2pp+1
-        hi[pp] = __builtin_amdgcn_perm(od, ev, 0x07060302u);  // high halves: dim 2w+1
-      }
-      const int r0 = dg * 8 + 2 * wd;
-      *reinterpret_cast<uint4*>(Vt + v_off(r0) + kg * 8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      *reinterpret_cast<uint4*>(Vt + v_off(r0 + 1) + kg * 8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16_t* Kt = lds + buf * kBuf;
-    bf16_t* Vt = Kt + kTileK;
-    if (do_k) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int id = st + 256 * i;
-        *reinterpret_cast<uint4*>(Kt + (id >> 4) * kRowK + (id & 15) * 8) = pk[i];
-      }
-    }
-    if (do_v) store_v(Vt, QG == 2 ? pv : pk);
-  };
   auto entry = [&](int t) -> int { return kDense ? (t | (kModeFull << 24) | (kModeFull << 26)) : tl[t]; };
 
-  if (ntile > 0) {
-    load_tile(entry(0) & 0xffffff);
-    store_tile(0);
-    if (ntile > 1) load_tile(entry(1) & 0xffffff);
-  }
-  __syncthreads();
+  auto load_tile = [&](int kb, unsigned char* Ks, unsigned char* Vs) {
+    const unsigned char* kt = kp + (size_t)kb * B * 256;
+    const unsigned char* vtile = vp + (size_t)kb * 256;
+    if ((kb + 1) * B <= dm.n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * wave + i;
+        dma16(kt + m * 1024, dk[i], Ks + m * 1024);
+      }
+    } else {  // ragged last tile: rows past the end re-read the last key (their scores are masked)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * wave + i;
+        const int r = 4 * m + (lane >> 4);
+        const int key = min(kb * B + r, dm.n - 1);
+        dma16_lane(kp + (size_t)key * 256 + (((lane & 15) ^ key_perm(r & 15)) << 4), Ks + m * 1024);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * wave + i;
+      dma16(vtile + (size_t)m * 4 * npad * 2, dv[i], Vs + m * 1024);
+    }
+  };
+
+  if (ntile > 0) load_tile(entry(0) & 0xffffff, sK0, sV0);
 
   for (int t = 0; t < ntile; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of tile t has landed in LDS
+    __builtin_amdgcn_s_barrier();         // every wave's share too; all waves are done with tile t - 1
+    if (t + 1 < ntile) {                  // refill the buffer of tile t - 1 with tile t + 1
+      if (t & 1) load_tile(entry(t + 1) & 0xffffff, sK0, sV0);
+      else load_tile(entry(t + 1) & 0xffffff, sK1, sV1);
+    }
     const int e = entry(t);
     const int kb = e & 0xffffff;
     const int mode = slot_on ? (e >> (24 + 2 * slot)) & 3 : 0;
-    const bool diag = kb == qb;
-    const bf16_t* Kt = lds + (t & 1) * kBuf;
-    const bf16_t* Vt = Kt + kTileK;
+    const unsigned char* Kt = (t & 1) ? sK1 : sK0;
+    const unsigned char* Vt = (t & 1) ? sV1 : sV0;
     if (mode) {
+      const bool diag = kb == qb;
       bool tile_bias = false;
       {
         const int base = (qb - kb) * B;
-        for (int t2 = 0; t2 < bias.count; ++t2) {
-          const int off = bias.offsets[(size_t)bh * bias.count + t2];
-          tile_bias |= off > base - B && off < base + B;
-        }
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) tile_bias |= boff[t2] > base - B && boff[t2] < base + B;
       }
       const bool masked = diag || mode != kModeFull || (kb + 1) * B > dm.n;
+      const bool slow = masked || tile_bias;
+      const float ksc = slow ? 1.0f : sl2;  // multiplier from stored scores to log2 units
+
+      f32x16 S[2];       // scores of quarters a and a + 1 (by parity)
+      unsigned P[2][8];  // packed bf16 probabilities of quarters a - 1 and a (by parity), [4 s2 + j]
+      auto qk = [&](int a) {
+        f32x16 acc;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {  // 64-key halves of the tile
-        f32x16 sacc[QG][2];
+        for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
 #pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2) {
+        for (int kc = 0; kc < 8; ++kc)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(Kt + koff[kc] + a * 32 * 256)),
+                                                        qreg[kc], acc, 0, 0, 0);
+        S[a & 1] = acc;
+      };
+      auto pv = [&](int a) {
 #pragma unroll
-          for (int qg = 0; qg < QG; ++qg)
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8_t Pb = as_bf16x8(make_uint4(P[a & 1][4 * s2 + 0], P[a & 1][4 * s2 + 1],
+                                                   P[a & 1][4 * s2 + 2], P[a & 1][4 * s2 + 3]));
 #pragma unroll
-            for (int x = 0; x < 16; ++x) sacc[qg][a2][x] = 0.0f;
-          const int a = 2 * kh + a2;
-#pragma unroll
-          for (int kc = 0; kc < 8; ++kc) {
-            const bf16x8_t A =
-                as_bf16x8(*reinterpret_cast<const uint4*>(Kt + kfrag + 32 * a * kRowK + 16 * kc));
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg)
-              sacc[qg][a2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qreg[qg][kc], sacc[qg][a2], 0, 0, 0);
-          }
+          for (int t2 = 0; t2 < 4; ++t2)
+            oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(lds_read16(Vt + voff[2 * a + s2] + t2 * 32 * 256)), Pb, oacc[t2], 0, 0, 0);
         }
-        const bool slow = masked || tile_bias;
-        unsigned pk2[QG][2][8];  // probabilities as packed bf16 pairs, per (a2, x / 2)
+      };
+      // masks / bias and the running max of quarter a; rescales O and l when needed
+      auto soft_max = [&](int a) -> float {
+        f32x16& s = S[a & 1];
+        if (slow) {
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-          // element (a2, x) of this lane is key column c = C + 8 hl of the tile with the
-          // compile-time C = 32 (2 kh + a2) + 16 (x >> 3) + (x & 7); its query row is r
-          if (slow) {
+          for (int x = 0; x < 16; ++x) s[x] *= sl2;
+          int rr = r_in_blk - 8 * hl;  // r >= c  <=>  rr >= C
+          asm volatile("" : "+v"(rr));
+          if (tile_bias) {
 #pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2)
+            for (int t2 = 0; t2 < 8; ++t2) {
+              if (boff[t2] < 0) continue;
+              const int cstar = rr - (boff[t2] - (qb - kb) * B);  // r - c == off  <=>  C == cstar
 #pragma unroll
-              for (int x = 0; x < 16; ++x) sacc[qg][a2][x] *= sl2;
-            int rr = r_in_blk[qg] - 8 * hl;  // r >= c  <=>  rr >= C
-            // keep the per-element compares inside the loop (hoisting them costs 256 SGPRs)
-            asm volatile("" : "+v"(rr));
-            if (tile_bias) {
-              for (int t2 = 0; t2 < bias.count; ++t2) {
-                const int off = bias.offsets[(size_t)bh * bias.count + t2];
-                const float bv = bias.values[(size_t)bh * bias.count + t2] * log2e;
-                const int cstar = rr - (off - (qb - kb) * B);  // r - c == off  <=>  C == cstar
-#pragma unroll
-                for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-                  for (int x = 0; x < 16; ++x)
-                    if (32 * (2 * kh + a2) + 16 * (x >> 3) + (x & 7) == cstar) sacc[qg][a2][x] += bv;
-              }
-            }
-            if (masked) {
-              const bool lower_ok = (mode & kModeLower) != 0;
-              const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
-              const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
-#pragma unroll
-              for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                  const int C = 32 * (2 * kh + a2) + 16 * (x >> 3) + (x & 7);
-                  const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
-                  if (!keep) sacc[qg][a2][x] = -__builtin_inff();
-                }
+              for (int x = 0; x < 16; ++x)
+                if (32 * a + 16 * (x >> 3) + (x & 7) == cstar) s[x] += bval[t2];
             }
           }
-          // row max of this half (raw scores on the fast path: the scale is positive)
-          float mx = -__builtin_inff();
+          if (masked) {
+            const bool lower_ok = (mode & kModeLower) != 0;
+            const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
+            const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
 #pragma unroll
-          for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-            for (int x = 0; x < 16; x += 2) mx = fmaxf(mx, fmaxf(sacc[qg][a2][x], sacc[qg][a2][x + 1]));
-          const float ksc = slow ? 1.0f : sl2;  // multiplier from stored scores to log2 units
-          mx *= ksc;
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          // lazy rescaling: the running max moves (and O, l are rescaled) only when
-          // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
-          if (__any(mx > m_run[qg] + 8.0f)) {
-            const float m_new = mx > m_run[qg] ? mx : m_run[qg];
-            const float alpha =
-                m_run[qg] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run[qg] - m_new);
-            m_run[qg] = m_new;
-            l_run[qg] *= alpha;
-#pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-              for (int x = 0; x < 16; ++x) oacc[qg][t2][x] *= alpha;
-          }
-          const float m_use = m_run[qg] == -__builtin_inff() ? 0.0f : m_run[qg];
-          float psum = l_run[qg];
-#pragma unroll
-          for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-            for (int x = 0; x < 16; x += 2) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qg][a2][x], ksc, -m_use));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qg][a2][x + 1], ksc, -m_use));
-              pk2[qg][a2][x >> 1] = pack_bf16x2(p0, p1);
-              psum = sum_bf16x2(pk2[qg][a2][x >> 1], psum);
-            }
-          l_run[qg] = psum;
-        }
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8_t P[QG];
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg)
-              P[qg] = as_bf16x8(make_uint4(pk2[qg][a2][4 * s2 + 0], pk2[qg][a2][4 * s2 + 1], pk2[qg][a2][4 * s2 + 2],
-                                           pk2[qg][a2][4 * s2 + 3]));
-            const int a = 2 * kh + a2;
-#pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2) {
-              // V^T rows 32 t2 + ql, keys 32 a + 16 s2 + 8 hl .. + 7
-              const bf16x8_t A = as_bf16x8(*reinterpret_cast<const uint4*>(
-                  Vt + vfrag + t2 * (32 * kRowV + 4 * 8) + 32 * a + 16 * s2));
-#pragma unroll
-              for (int qg = 0; qg < QG; ++qg)
-                oacc[qg][t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[qg], oacc[qg][t2], 0, 0, 0);
+            for (int x = 0; x < 16; ++x) {
+              const int C = 32 * a + 16 * (x >> 3) + (x & 7);
+              const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
+              if (!keep) s[x] = -__builtin_inff();
             }
           }
         }
+        float mx = s[0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[x]);
+        mx *= ksc;
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // lazy rescaling: the running max moves (and O, l are rescaled) only when
+        // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
+        if (__any(mx > m_run + 8.0f)) {
+          const float m_new = mx > m_run ? mx : m_run;
+          const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) oacc[t2][x] *= alpha;
+        }
+        return m_run == -__builtin_inff() ? 0.0f : m_run;
+      };
+      // probabilities of quarter a as packed bf16, row sums from the same bf16 values
+      auto soft_exp = [&](int a, float m_use) {
+        float psum = l_run;
+#pragma unroll
+        for (int x = 0; x < 16; x += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
+          P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
+          psum = sum_bf16x2(P[a & 1][x >> 1], psum);
+        }
+        l_run = psum;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pin(P[a & 1][j]);
+      };
+
+      qk(0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float m_use = soft_max(a);
+        if (a < 3) qk(a + 1);
+        if (a > 0) pv(a - 1);
+        soft_exp(a, m_use);
       }
+      pv(3);
     }
-    if (t + 1 < ntile) {
-      store_tile((t + 1) & 1);
-      if (t + 2 < ntile) load_tile(entry(t + 2) & 0xffffff);
-    }
-    __syncthreads();
   }
 
-  if (!slot_on) return;
+  if (!slot_on || qrow >= dm.n) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  bf16_t* op = o + ((size_t)bh * dm.n + qrow) * D;
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    if (qrow[qg] >= dm.n) continue;
-    const float l_tot = l_run[qg] + __shfl_xor(l_run[qg], 32);
-    const float inv = 1.0f / l_tot;
-    bf16_t* op = o + ((size_t)bh * dm.n + qrow[qg]) * D;
+  for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2)
+    for (int gg = 0; gg < 4; ++gg) {
+      const int d0 = 32 * t2 + 8 * gg + 4 * hl;
+      uint2 wv;
+      wv.x = pack_bf16x2(oacc[t2][4 * gg + 0] * inv, oacc[t2][4 * gg + 1] * inv);
+      wv.y = pack_bf16x2(oacc[t2][4 * gg + 2] * inv, oacc[t2][4 * gg + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d0) = wv;
+    }
+}
+
+// V^T of one KV head with keys padded to npad (a multiple of B) with zeros:
+// vt[kvh][dim][key].  Block = 64 keys x 128 dims.
+__global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restrict__ v, bf16_t* __restrict__ vt,
+                                                          int n, int npad) {
+  __shared__ unsigned short tile[64][130];
+  const int kvh = blockIdx.y, k0 = blockIdx.x * 64, tid = threadIdx.x;
+  const bf16_t* src = v + (size_t)kvh * n * 128;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int d0 = 32 * t2 + 8 * gg + 4 * hl;
-        uint2 wv;
-        wv.x = pack_bf16x2(oacc[qg][t2][4 * gg + 0] * inv, oacc[qg][t2][4 * gg + 1] * inv);
-        wv.y = pack_bf16x2(oacc[qg][t2][4 * gg + 2] * inv, oacc[qg][t2][4 * gg + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d0) = wv;
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i;  // 1024 chunks of 8 dims
+    const int key = id >> 4, c = id & 15;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (k0 + key < n) u = *reinterpret_cast<const uint4*>(src + (size_t)(k0 + key) * 128 + c * 8);
+    const unsigned w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[key][c * 8 + 2 * j] = (unsigned short)(w4[j] & 0xffffu);
+      tile[key][c * 8 + 2 * j + 1] = (unsigned short)(w4[j] >> 16);
+    }
+  }
+  __syncthreads();
+  bf16_t* dst = vt + (size_t)kvh * 128 * npad + k0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + 256 * i;  // 1024 chunks of 8 keys
+    const int dim = id >> 3, c = id & 7;
+    unsigned w4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w4[j] = (unsigned)tile[c * 8 + 2 * j][dim] | ((unsigned)tile[c * 8 + 2 * j + 1][dim] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)dim * npad + c * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
 }
 
@@ -598,19 +608,20 @@ hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, in
 
 hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q, const void* k,
                             const void* v, void* o, const int* tiles, const int* tile_cnt, const int* ulist,
-                            const int* ucnt, hipStream_t st) {
+                            const int* ucnt, void* vt, hipStream_t st) {
   if (use_matrix_engine(dm)) {
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
-    const bf16_t* vv = static_cast<const bf16_t*>(v);
+    bf16_t* vvt = static_cast<bf16_t*>(vt);
     bf16_t* oo = static_cast<bf16_t*>(o);
+    const int npad = dm.nb * dm.B;
+    transpose_v_kernel<<<dim3(npad / 64, dm.bkv), 256, 0, st>>>(static_cast<const bf16_t*>(v), vvt, dm.n, npad);
     const int pairs = (dm.group + 1) / 2;
     const int items = dm.bkv * pairs * dm.nb;
-    constexpr int QG = CRISP_ATTN_QG;
     if (tiles == nullptr)
-      attn_mfma_kernel<true, QG><<<items, 512 / QG, 0, st>>>(qq, kk, vv, oo, dm, bias, nullptr, nullptr, pairs);
+      attn_mfma_kernel<true><<<items, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, nullptr, nullptr, pairs, npad);
     else
-      attn_mfma_kernel<false, QG><<<items, 512 / QG, 0, st>>>(qq, kk, vv, oo, dm, bias, ulist, ucnt, pairs);
+      attn_mfma_kernel<false><<<items, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, ulist, ucnt, pairs, npad);
   } else if (dm.dtype == 1) {
     if (dm.d == 128) launch_generic<bf16_t, 128>(dm, bias, q, k, v, o, tiles, tile_cnt, st);
     else launch_generic<bf16_t, 64>(dm, bias, q, k, v, o, tiles, tile_cnt, st);

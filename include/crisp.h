@@ -121,8 +121,9 @@ typedef struct {
   int64_t pe_cap;       /* per-head capacity of pe_col, >= crisp_index_capacity() */
 } crisp_index_sets;
 
-/* Scratch bytes needed by crisp_route, crisp_select_indices and
- * crisp_sparse_prefill for this shape (0 if the arguments are invalid). */
+/* Scratch bytes needed by crisp_route, crisp_select_indices,
+ * crisp_sparse_prefill and crisp_dense_prefill for this shape (0 if the
+ * arguments are invalid). */
 size_t crisp_workspace_size(const crisp_shape* shape, const crisp_config* cfg);
 
 /* Per-head capacity pe_col needs: N_b (N_b + 1) / 2 (-1 if invalid). */
@@ -158,10 +159,11 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
                                   const crisp_index_sets* idx, void* ws, size_t ws_bytes, void* o,
                                   void* stream);
 
-/* Full causal attention (the dense baseline; same tile engine).  Writes o. */
+/* Full causal attention (the dense baseline; same tile engine).  Reads q, k,
+ * v, bias; uses ws as scratch; writes o. */
 crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
-                                 const void* k, const void* v, const crisp_rel_bias* bias, void* o,
-                                 void* stream);
+                                 const void* k, const void* v, const crisp_rel_bias* bias, void* ws,
+                                 size_t ws_bytes, void* o, void* stream);
 
 /* Static description of a status code. */
 const char* crisp_status_string(crisp_status status);

@@ -111,10 +111,11 @@ def run_sparse(spec, X: DeviceInputs, bufs: crisp.Buffers):
     return o
 
 
-def run_dense(spec, X: DeviceInputs):
+def run_dense(spec, X: DeviceInputs, bufs: crisp.Buffers = None):
     import torch
     o = torch.empty_like(X.q)
-    crisp.dense_prefill(spec, X.q, X.k, X.v, o, X.bias_offsets, X.bias_values)
+    crisp.dense_prefill(spec, X.q, X.k, X.v, o, bufs if bufs is not None else crisp.Buffers(spec), X.bias_offsets,
+                        X.bias_values)
     torch.cuda.synchronize()
     return o
 

@@ -69,7 +69,7 @@ def test_validation_errors(lib, kw, code):
                          ctypes.byref(idx), None)
     assert rc == code
     rc = lib.crisp_dense_prefill(ctypes.byref(s.shape()), ctypes.byref(s.config()), fake, fake, fake, None, fake,
-                                 None)
+                                 1 << 40, fake, None)
     assert rc == code
 
 
@@ -94,6 +94,8 @@ def test_null_alignment_workspace_capacity(lib):
     nb = crisp.RelBias(2, None, 1 << 20)
     assert lib.crisp_sparse_prefill(sh, cf, fake, fake, fake, ctypes.byref(nb), ctypes.byref(idx), fake, ws, fake,
                                     None) == -1
+    assert lib.crisp_dense_prefill(sh, cf, fake, fake, fake, None, fake, ws - 1, fake, None) == -5
+    assert lib.crisp_dense_prefill(sh, cf, fake, fake, fake, None, None, ws, fake, None) == -1
 
 
 def test_status_strings(lib):
