@@ -19,6 +19,8 @@
 // K side to make that layout line up).  K is staged in LDS row-major, V is
 // transposed in registers (8 x 8 bf16 blocks) while being staged, so every
 // LDS read feeding a matrix instruction is one 16-byte vector.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -93,7 +95,9 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
@@ -105,6 +109,16 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float sum_bf16x2(unsigned pr, float acc) {
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pr), one, acc, false);
+}
+
+// max / sum over the two 32-lane halves of the wave (v_permlane32_swap exchanges them)
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // key row inside a 32-key group that feeds matrix row rho (swap of bits 2 and 3)
@@ -121,24 +135,36 @@ __device__ __forceinline__ int key_perm(int rho) {
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-__device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, const void* lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+__device__ __forceinline__ unsigned uniform(unsigned x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const unsigned char* uniform(const unsigned char* p) {
+  const unsigned long long v = (unsigned long long)p;
+  return (const unsigned char*)(((unsigned long long)uniform((unsigned)(v >> 32)) << 32) | uniform((unsigned)v));
+}
+// lds_wave + kBufImm addresses the slot: lds_wave is a per-wave scalar, the
+// constant part is encoded in the instruction stream.
+template <unsigned kLdsConst>
+__device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, unsigned lds_wave) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(base), "s"(lds_addr(lds_base))
+               : "v"(voff), "s"(base), "s"(lds_wave), "n"(kLdsConst)
                : "memory", "m0");
 }
 // the same with a per-lane 64-bit address
-__device__ __forceinline__ void dma16_lane(const unsigned char* addr, const void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+template <unsigned kLdsConst>
+__device__ __forceinline__ void dma16_lane(const unsigned char* addr, unsigned lds_wave) {
+  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(addr), "s"(lds_addr(lds_base))
+               : "v"(addr), "s"(lds_wave), "n"(kLdsConst)
                : "memory", "m0");
 }
 
 // keeps a value materialised at this point (no sinking past later branches)
 __device__ __forceinline__ void pin(unsigned x) { asm volatile("" ::"v"(x)); }
 
-__device__ __forceinline__ uint4 lds_read16(const unsigned char* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte LDS reads through address-space-3 pointers: a per-lane base pointer plus a
+// constant element offset folds into the instruction's offset field
+typedef const __attribute__((address_space(3))) u32x4_t lds_u4;
+__device__ __forceinline__ lds_u4* lds_u4_ptr(const void* p) { return (lds_u4*)p; }
 
 // Work item of the matrix engine: (KV head g, pair w of its query heads, query
 // block qb).  Items are ordered by query block, heaviest first; inside a level
@@ -180,10 +206,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
                                                            const int* __restrict__ ulist,
                                                            const int* __restrict__ ucnt, int pairs, int npad) {
   constexpr int B = 128, D = 128;
-  __shared__ __align__(1024) unsigned char sK0[kTileBytes];
-  __shared__ __align__(1024) unsigned char sK1[kTileBytes];
-  __shared__ __align__(1024) unsigned char sV0[kTileBytes];
-  __shared__ __align__(1024) unsigned char sV1[kTileBytes];
+  // four tile buffers: K of even / odd tiles, then V^T of even / odd tiles
+  __shared__ __align__(1024) unsigned char smem[4 * kTileBytes];
 
   int qb, g, w;
   pair_item(dm, pairs, blockIdx.x, &qb, &g, &w);
@@ -218,81 +242,90 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
   const float sl2 = (float)(1.0 / __builtin_sqrt(128.0)) * log2e;
 
   // per-lane byte offsets of the matrix operands inside a tile
-  int koff[8], voff[8];
+  // (LDS byte addresses in the first buffer of each kind; the other buffer and the
+  // 32-row groups are constant offsets)
+  lds_u4* koff[8];
+  lds_u4* voff[8];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) koff[kc] = key_perm(ql) * 256 + (((2 * kc + hl) ^ l15) << 4);
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = lds_u4_ptr(smem) + key_perm(ql) * 16 + ((2 * kc + hl) ^ l15);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) voff[j] = ql * 256 + (((2 * j + hl) ^ l15) << 4);  // j = 2 a + s2
+  for (int j = 0; j < 8; ++j)  // j = 2 a + s2
+    voff[j] = lds_u4_ptr(smem + 2 * kTileBytes) + ql * 16 + ((2 * j + hl) ^ l15);
   // per-lane source offsets of the direct loads: instruction i of the wave fills
   // rows 4 m .. 4 m + 3 of a tile, m = 4 wave + i
   unsigned dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = 4 * i + (lane >> 4);
-    dk[i] = (lane >> 4) * 256 + (((lane & 15) ^ key_perm(rr)) << 4);
-    dv[i] = (lane >> 4) * npad * 2 + (((lane & 15) ^ rr) << 4);
+    const unsigned m = 4 * wave + i;
+    dk[i] = m * 1024 + (lane >> 4) * 256 + (((lane & 15) ^ key_perm(rr)) << 4);
+    dv[i] = m * 4 * npad * 2 + (lane >> 4) * npad * 2 + (((lane & 15) ^ rr) << 4);
   }
+  const unsigned lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4096);
 
-  // this head's relative-position bias (at most 8 offsets), held in scalar registers
+  // this head's relative-position bias (at most 8 offsets)
   int boff[8];
   float bval[8];
 #pragma unroll
   for (int t2 = 0; t2 < 8; ++t2) {
     boff[t2] = t2 < bias.count ? __builtin_amdgcn_readfirstlane(bias.offsets[(size_t)bh * bias.count + t2]) : -1;
-    bval[t2] = t2 < bias.count
-                   ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                         int, bias.values[(size_t)bh * bias.count + t2] * log2e)))
-                   : 0.0f;
+    bval[t2] = t2 < bias.count ? bias.values[(size_t)bh * bias.count + t2] * log2e : 0.0f;
   }
+
+  int bias_dmax = -1;  // largest query-block minus key-block distance a bias offset reaches
+#pragma unroll
+  for (int t2 = 0; t2 < 8; ++t2)
+    if (boff[t2] >= 0) bias_dmax = max(bias_dmax, (boff[t2] + B - 1) / B);
 
   const int item = g * pairs + w;
   const int ntile = kDense ? qb + 1 : ucnt[(size_t)item * dm.nb + qb];
   const int* tl = kDense ? nullptr : ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
   auto entry = [&](int t) -> int { return kDense ? (t | (kModeFull << 24) | (kModeFull << 26)) : tl[t]; };
 
-  auto load_tile = [&](int kb, unsigned char* Ks, unsigned char* Vs) {
+  // K tile -> buffer KI, V^T tile -> buffer 2 + KI (KI a compile-time 0 / 1)
+  auto load_tile = [&](int kb, auto KI) {
+    constexpr unsigned kK = decltype(KI)::value * kTileBytes, kV = (2 + decltype(KI)::value) * kTileBytes;
     const unsigned char* kt = kp + (size_t)kb * B * 256;
     const unsigned char* vtile = vp + (size_t)kb * 256;
     if ((kb + 1) * B <= dm.n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * wave + i;
-        dma16(kt + m * 1024, dk[i], Ks + m * 1024);
-      }
+      dma16<kK + 0 * 1024>(kt, dk[0], lds_wave);
+      dma16<kK + 1 * 1024>(kt, dk[1], lds_wave);
+      dma16<kK + 2 * 1024>(kt, dk[2], lds_wave);
+      dma16<kK + 3 * 1024>(kt, dk[3], lds_wave);
     } else {  // ragged last tile: rows past the end re-read the last key (their scores are masked)
+      const unsigned char* a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 4 * wave + i;
-        const int r = 4 * m + (lane >> 4);
+        const int r = 4 * (4 * wave + i) + (lane >> 4);
         const int key = min(kb * B + r, dm.n - 1);
-        dma16_lane(kp + (size_t)key * 256 + (((lane & 15) ^ key_perm(r & 15)) << 4), Ks + m * 1024);
+        a[i] = kp + (size_t)key * 256 + (((lane & 15) ^ key_perm(r & 15)) << 4);
       }
+      dma16_lane<kK + 0 * 1024>(a[0], lds_wave);
+      dma16_lane<kK + 1 * 1024>(a[1], lds_wave);
+      dma16_lane<kK + 2 * 1024>(a[2], lds_wave);
+      dma16_lane<kK + 3 * 1024>(a[3], lds_wave);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * wave + i;
-      dma16(vtile + (size_t)m * 4 * npad * 2, dv[i], Vs + m * 1024);
-    }
+    dma16<kV + 0 * 1024>(vtile, dv[0], lds_wave);
+    dma16<kV + 1 * 1024>(vtile, dv[1], lds_wave);
+    dma16<kV + 2 * 1024>(vtile, dv[2], lds_wave);
+    dma16<kV + 3 * 1024>(vtile, dv[3], lds_wave);
   };
 
-  if (ntile > 0) load_tile(entry(0) & 0xffffff, sK0, sV0);
-
-  for (int t = 0; t < ntile; ++t) {
+  // One tile: wait for its loads (issued one tile earlier), start the loads of
+  // the next tile into the other buffer, compute.  Called with the buffers as
+  // constants so every LDS address is a per-lane base plus an immediate.
+  auto tile_step = [&](int t, auto KI) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of tile t has landed in LDS
     __builtin_amdgcn_s_barrier();         // every wave's share too; all waves are done with tile t - 1
-    if (t + 1 < ntile) {                  // refill the buffer of tile t - 1 with tile t + 1
-      if (t & 1) load_tile(entry(t + 1) & 0xffffff, sK0, sV0);
-      else load_tile(entry(t + 1) & 0xffffff, sK1, sV1);
-    }
+    if (t + 1 < ntile) load_tile(entry(t + 1) & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
+    constexpr int kbo = decltype(KI)::value * kTileBytes / 16, vbo = kbo;
     const int e = entry(t);
     const int kb = e & 0xffffff;
     const int mode = slot_on ? (e >> (24 + 2 * slot)) & 3 : 0;
-    const unsigned char* Kt = (t & 1) ? sK1 : sK0;
-    const unsigned char* Vt = (t & 1) ? sV1 : sV0;
     if (mode) {
       const bool diag = kb == qb;
       bool tile_bias = false;
-      {
+      if (qb - kb <= bias_dmax) {
         const int base = (qb - kb) * B;
 #pragma unroll
         for (int t2 = 0; t2 < 8; ++t2) tile_bias |= boff[t2] > base - B && boff[t2] < base + B;
@@ -309,7 +342,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
         for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_read16(Kt + koff[kc] + a * 32 * 256)),
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(koff[kc][kbo + a * 32 * 16]),
                                                         qreg[kc], acc, 0, 0, 0);
         S[a & 1] = acc;
       };
@@ -321,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
 #pragma unroll
           for (int t2 = 0; t2 < 4; ++t2)
             oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(lds_read16(Vt + voff[2 * a + s2] + t2 * 32 * 256)), Pb, oacc[t2], 0, 0, 0);
+                as_bf16x8(voff[2 * a + s2][vbo + t2 * 32 * 16]), Pb, oacc[t2], 0, 0, 0);
         }
       };
       // masks / bias and the running max of quarter a; rescales O and l when needed
@@ -358,7 +391,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
 #pragma unroll
         for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[x]);
         mx *= ksc;
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = half_swap_max(mx);
         // lazy rescaling: the running max moves (and O, l are rescaled) only when
         // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
         if (__any(mx > m_run + 8.0f)) {
@@ -398,10 +431,16 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
       }
       pv(3);
     }
+  };
+
+  if (ntile > 0) load_tile(entry(0) & 0xffffff, std::integral_constant<int, 0>());
+  for (int t = 0; t < ntile; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>());
+    if (t + 1 < ntile) tile_step(t + 1, std::integral_constant<int, 1>());
   }
 
   if (!slot_on || qrow >= dm.n) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_swap_sum(l_run);
   const float inv = 1.0f / l_tot;
   bf16_t* op = o + ((size_t)bh * dm.n + qrow) * D;
 #pragma unroll
