@@ -25,7 +25,7 @@ struct Layout {
   // select
   size_t s_qbar, s_kbar, s_zbar, s_abar, s_rowtot, s_hist, s_state, s_gt, s_tie, s_tiep, s_end;
   // attention
-  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_vt, a_end;
+  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_vt, a_qcnt, a_end;
   size_t total;
 };
 
@@ -110,6 +110,8 @@ Layout layout(const Dims& d) {
   o = align_up(o + pairs * d.nb * sizeof(int));
   L.a_vt = o;
   if (use_matrix_engine(d)) o = align_up(o + (size_t)d.bkv * d.d * d.nb * d.B * 2);  // V^T, bf16
+  L.a_qcnt = o;
+  o = align_up(o + 8 * sizeof(int));  // work-queue counters
   L.a_end = o;
 
   L.total = L.r_end;
@@ -290,7 +292,8 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (launch_build_tiles(d, index_out(idx), tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
-  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, w + L.a_vt, st) != hipSuccess)
+  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, w + L.a_vt,
+                       reinterpret_cast<int*>(w + L.a_qcnt), st) != hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }
@@ -312,7 +315,7 @@ crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* c
   char* w = static_cast<char*>(ws);
   (void)hipGetLastError();
   if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, nullptr, nullptr, w + L.a_vt,
-                       static_cast<hipStream_t>(stream)) != hipSuccess)
+                       reinterpret_cast<int*>(w + L.a_qcnt), static_cast<hipStream_t>(stream)) != hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }

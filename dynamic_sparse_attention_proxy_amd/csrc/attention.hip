@@ -166,18 +166,15 @@ __device__ __forceinline__ void pin(unsigned x) { asm volatile("" ::"v"(x)); }
 typedef const __attribute__((address_space(3))) u32x4_t lds_u4;
 __device__ __forceinline__ lds_u4* lds_u4_ptr(const void* p) { return (lds_u4*)p; }
 
-// Work item of the matrix engine: (KV head g, pair w of its query heads, query
-// block qb).  Items are ordered by query block, heaviest first; inside a level
-// the pairs of one KV head are 8 items apart so they land on the same XCD
-// (shared K/V in its L2), and the KV head served by an XCD rotates with the
-// level so that cheap (VS) and expensive (PE) groups alternate on every XCD.
-__device__ __forceinline__ void pair_item(const Dims& dm, int pairs, int L, int* qb, int* g, int* w) {
-  const int U = dm.bkv * pairs;
-  const int level = L / U, p = L % U;
-  *w = p / dm.bkv;
-  *g = (p % dm.bkv + level) % dm.bkv;
-  *qb = dm.nb - 1 - level;
-}
+// Work items of the matrix engine are (KV head g, pair w of its query heads,
+// query block qb).  The combos c = g * pairs + w are split into 8 contiguous
+// runs, one per XCD queue, so that the workgroups of an XCD share the K/V
+// stream of one KV head in that XCD's L2.  A queue lists its items by query
+// block, heaviest first.  A workgroup takes items from the queue of its own XCD
+// and, once that is empty, from the others (load balance between cheap and
+// expensive heads).
+// Queue i owns combos combos * i / 8 .. combos * (i + 1) / 8 - 1.
+__device__ __forceinline__ int queue_begin(int combos, int i) { return (int)((long long)combos * i / 8); }
 
 // LDS tiles are 128 rows of 256 bytes; the sixteen 16-byte chunks of a row are
 // stored XOR-swizzled so that the 16 lanes of a matrix-operand read (16
@@ -204,42 +201,20 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ vt,
                                                            bf16_t* __restrict__ o, Dims dm, BiasArgs bias,
                                                            const int* __restrict__ ulist,
-                                                           const int* __restrict__ ucnt, int pairs, int npad) {
+                                                           const int* __restrict__ ucnt, int pairs, int npad,
+                                                           int* __restrict__ counters) {
   constexpr int B = 128, D = 128;
   // four tile buffers: K of even / odd tiles, then V^T of even / odd tiles
   __shared__ __align__(1024) unsigned char smem[4 * kTileBytes];
+  __shared__ int s_item;
 
-  int qb, g, w;
-  pair_item(dm, pairs, blockIdx.x, &qb, &g, &w);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave-level addresses scalar
   const int slot = wave >> 2;
   const int hl = lane >> 5, ql = lane & 31, l15 = lane & 15;
-  const int bidx = g / dm.hkv, gh = g % dm.hkv;
-  const int hin = 2 * w + slot;
-  const bool slot_on = hin < dm.group;
-  const int bh = bidx * dm.hq + gh * dm.group + (slot_on ? hin : 0);
-  const bf16_t* qp = q + (size_t)bh * dm.n * D;
-  const unsigned char* kp = reinterpret_cast<const unsigned char*>(k + (size_t)g * dm.n * D);
-  const unsigned char* vp = reinterpret_cast<const unsigned char*>(vt + (size_t)g * D * npad);
-  const int r_in_blk = (wave & 3) * 32 + ql;
-  const int qrow = qb * B + r_in_blk;
-
-  bf16x8_t qreg[8];
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (slot_on && qrow < dm.n) u = *reinterpret_cast<const uint4*>(qp + (size_t)qrow * D + 16 * kc + 8 * hl);
-    qreg[kc] = as_bf16x8(u);
-  }
-  f32x16 oacc[4];
-#pragma unroll
-  for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[t2][e] = 0.0f;
-  float m_run = -__builtin_inff(), l_run = 0.0f;
   const float log2e = 1.4426950408889634f;
   const float sl2 = (float)(1.0 / __builtin_sqrt(128.0)) * log2e;
+  const int r_in_blk = (wave & 3) * 32 + ql;
 
   // per-lane byte offsets of the matrix operands inside a tile
   // (LDS byte addresses in the first buffer of each kind; the other buffer and the
@@ -262,197 +237,247 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
     dv[i] = m * 4 * npad * 2 + (lane >> 4) * npad * 2 + (((lane & 15) ^ rr) << 4);
   }
   const unsigned lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4096);
+  const int xcd = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // hardware XCC id (4 bits)
+  const int combos = dm.bkv * pairs;
 
-  // this head's relative-position bias (at most 8 offsets)
-  int boff[8];
-  float bval[8];
-#pragma unroll
-  for (int t2 = 0; t2 < 8; ++t2) {
-    boff[t2] = t2 < bias.count ? __builtin_amdgcn_readfirstlane(bias.offsets[(size_t)bh * bias.count + t2]) : -1;
-    bval[t2] = t2 < bias.count ? bias.values[(size_t)bh * bias.count + t2] * log2e : 0.0f;
-  }
-
-  int bias_dmax = -1;  // largest query-block minus key-block distance a bias offset reaches
-#pragma unroll
-  for (int t2 = 0; t2 < 8; ++t2)
-    if (boff[t2] >= 0) bias_dmax = max(bias_dmax, (boff[t2] + B - 1) / B);
-
-  const int item = g * pairs + w;
-  const int ntile = kDense ? qb + 1 : ucnt[(size_t)item * dm.nb + qb];
-  const int* tl = kDense ? nullptr : ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
-  auto entry = [&](int t) -> int { return kDense ? (t | (kModeFull << 24) | (kModeFull << 26)) : tl[t]; };
-
-  // K tile -> buffer KI, V^T tile -> buffer 2 + KI (KI a compile-time 0 / 1)
-  auto load_tile = [&](int kb, auto KI) {
-    constexpr unsigned kK = decltype(KI)::value * kTileBytes, kV = (2 + decltype(KI)::value) * kTileBytes;
-    const unsigned char* kt = kp + (size_t)kb * B * 256;
-    const unsigned char* vtile = vp + (size_t)kb * 256;
-    if ((kb + 1) * B <= dm.n) {
-      dma16<kK + 0 * 1024>(kt, dk[0], lds_wave);
-      dma16<kK + 1 * 1024>(kt, dk[1], lds_wave);
-      dma16<kK + 2 * 1024>(kt, dk[2], lds_wave);
-      dma16<kK + 3 * 1024>(kt, dk[3], lds_wave);
-    } else {  // ragged last tile: rows past the end re-read the last key (their scores are masked)
-      const unsigned char* a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * (4 * wave + i) + (lane >> 4);
-        const int key = min(kb * B + r, dm.n - 1);
-        a[i] = kp + (size_t)key * 256 + (((lane & 15) ^ key_perm(r & 15)) << 4);
+  for (;;) {
+    // next item: own queue first, then the others in turn
+    if (tid == 0) {
+      int it = -1;
+      for (int k2 = 0; k2 < 8 && it < 0; ++k2) {
+        const int qi = (xcd + k2) & 7;
+        const int n_items = (queue_begin(combos, qi + 1) - queue_begin(combos, qi)) * dm.nb;
+        if (n_items == 0 || __hip_atomic_load(&counters[qi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_items)
+          continue;
+        const int v = atomicAdd(&counters[qi], 1);
+        if (v < n_items) it = (qi << 24) | v;
       }
-      dma16_lane<kK + 0 * 1024>(a[0], lds_wave);
-      dma16_lane<kK + 1 * 1024>(a[1], lds_wave);
-      dma16_lane<kK + 2 * 1024>(a[2], lds_wave);
-      dma16_lane<kK + 3 * 1024>(a[3], lds_wave);
+      s_item = it;
     }
-    dma16<kV + 0 * 1024>(vtile, dv[0], lds_wave);
-    dma16<kV + 1 * 1024>(vtile, dv[1], lds_wave);
-    dma16<kV + 2 * 1024>(vtile, dv[2], lds_wave);
-    dma16<kV + 3 * 1024>(vtile, dv[3], lds_wave);
-  };
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    if (it < 0) break;
+    const int qi = it >> 24, v = it & 0xffffff;
+    const int c0 = queue_begin(combos, qi), ncomb = queue_begin(combos, qi + 1) - c0;
+    const int comb = c0 + v % ncomb;
+    const int qb = dm.nb - 1 - v / ncomb, g = comb / pairs, w = comb % pairs;
 
-  // One tile: wait for its loads (issued one tile earlier), start the loads of
-  // the next tile into the other buffer, compute.  Called with the buffers as
-  // constants so every LDS address is a per-lane base plus an immediate.
-  auto tile_step = [&](int t, auto KI) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of tile t has landed in LDS
-    __builtin_amdgcn_s_barrier();         // every wave's share too; all waves are done with tile t - 1
-    if (t + 1 < ntile) load_tile(entry(t + 1) & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
-    constexpr int kbo = decltype(KI)::value * kTileBytes / 16, vbo = kbo;
-    const int e = entry(t);
-    const int kb = e & 0xffffff;
-    const int mode = slot_on ? (e >> (24 + 2 * slot)) & 3 : 0;
-    if (mode) {
-      const bool diag = kb == qb;
-      bool tile_bias = false;
-      if (qb - kb <= bias_dmax) {
-        const int base = (qb - kb) * B;
-#pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2) tile_bias |= boff[t2] > base - B && boff[t2] < base + B;
-      }
-      const bool masked = diag || mode != kModeFull || (kb + 1) * B > dm.n;
-      const bool slow = masked || tile_bias;
-      const float ksc = slow ? 1.0f : sl2;  // multiplier from stored scores to log2 units
+    const int bidx = g / dm.hkv, gh = g % dm.hkv;
+    const int hin = 2 * w + slot;
+    const bool slot_on = hin < dm.group;
+    const int bh = bidx * dm.hq + gh * dm.group + (slot_on ? hin : 0);
+    const bf16_t* qp = q + (size_t)bh * dm.n * D;
+    const unsigned char* kp = reinterpret_cast<const unsigned char*>(k + (size_t)g * dm.n * D);
+    const unsigned char* vp = reinterpret_cast<const unsigned char*>(vt + (size_t)g * D * npad);
+    const int qrow = qb * B + r_in_blk;
 
-      f32x16 S[2];       // scores of quarters a and a + 1 (by parity)
-      unsigned P[2][8];  // packed bf16 probabilities of quarters a - 1 and a (by parity), [4 s2 + j]
-      auto qk = [&](int a) {
-        f32x16 acc;
+    bf16x8_t qreg[8];
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
+    for (int kc = 0; kc < 8; ++kc) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (slot_on && qrow < dm.n) u = *reinterpret_cast<const uint4*>(qp + (size_t)qrow * D + 16 * kc + 8 * hl);
+      qreg[kc] = as_bf16x8(u);
+    }
+    f32x16 oacc[4];
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(koff[kc][kbo + a * 32 * 16]),
-                                                        qreg[kc], acc, 0, 0, 0);
-        S[a & 1] = acc;
-      };
-      auto pv = [&](int a) {
+    for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8_t Pb = as_bf16x8(make_uint4(P[a & 1][4 * s2 + 0], P[a & 1][4 * s2 + 1],
-                                                   P[a & 1][4 * s2 + 2], P[a & 1][4 * s2 + 3]));
+      for (int e = 0; e < 16; ++e) oacc[t2][e] = 0.0f;
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+
+    // this head's relative-position bias (at most 8 offsets)
+    int boff[8];
+    float bval[8];
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2)
-            oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(voff[2 * a + s2][vbo + t2 * 32 * 16]), Pb, oacc[t2], 0, 0, 0);
+    for (int t2 = 0; t2 < 8; ++t2) {
+      boff[t2] = t2 < bias.count ? __builtin_amdgcn_readfirstlane(bias.offsets[(size_t)bh * bias.count + t2]) : -1;
+      bval[t2] = t2 < bias.count ? bias.values[(size_t)bh * bias.count + t2] * log2e : 0.0f;
+    }
+
+    int bias_dmax = -1;  // largest query-block minus key-block distance a bias offset reaches
+#pragma unroll
+    for (int t2 = 0; t2 < 8; ++t2)
+      if (boff[t2] >= 0) bias_dmax = max(bias_dmax, (boff[t2] + B - 1) / B);
+
+    const int item = g * pairs + w;
+    const int ntile = kDense ? qb + 1 : ucnt[(size_t)item * dm.nb + qb];
+    const int* tl = kDense ? nullptr : ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
+    auto entry = [&](int t) -> int { return kDense ? (t | (kModeFull << 24) | (kModeFull << 26)) : tl[t]; };
+
+    // K tile -> buffer KI, V^T tile -> buffer 2 + KI (KI a compile-time 0 / 1)
+    auto load_tile = [&](int kb, auto KI) {
+      constexpr unsigned kK = decltype(KI)::value * kTileBytes, kV = (2 + decltype(KI)::value) * kTileBytes;
+      const unsigned char* kt = kp + (size_t)kb * B * 256;
+      const unsigned char* vtile = vp + (size_t)kb * 256;
+      if ((kb + 1) * B <= dm.n) {
+        dma16<kK + 0 * 1024>(kt, dk[0], lds_wave);
+        dma16<kK + 1 * 1024>(kt, dk[1], lds_wave);
+        dma16<kK + 2 * 1024>(kt, dk[2], lds_wave);
+        dma16<kK + 3 * 1024>(kt, dk[3], lds_wave);
+      } else {  // ragged last tile: rows past the end re-read the last key (their scores are masked)
+        const unsigned char* a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * (4 * wave + i) + (lane >> 4);
+          const int key = min(kb * B + r, dm.n - 1);
+          a[i] = kp + (size_t)key * 256 + (((lane & 15) ^ key_perm(r & 15)) << 4);
         }
-      };
-      // masks / bias and the running max of quarter a; rescales O and l when needed
-      auto soft_max = [&](int a) -> float {
-        f32x16& s = S[a & 1];
-        if (slow) {
+        dma16_lane<kK + 0 * 1024>(a[0], lds_wave);
+        dma16_lane<kK + 1 * 1024>(a[1], lds_wave);
+        dma16_lane<kK + 2 * 1024>(a[2], lds_wave);
+        dma16_lane<kK + 3 * 1024>(a[3], lds_wave);
+      }
+      dma16<kV + 0 * 1024>(vtile, dv[0], lds_wave);
+      dma16<kV + 1 * 1024>(vtile, dv[1], lds_wave);
+      dma16<kV + 2 * 1024>(vtile, dv[2], lds_wave);
+      dma16<kV + 3 * 1024>(vtile, dv[3], lds_wave);
+    };
+
+    // One tile: wait for its loads (issued one tile earlier), start the loads of
+    // the next tile into the other buffer, compute.  Called with the buffers as
+    // constants so every LDS address is a per-lane base plus an immediate.
+    auto tile_step = [&](int t, auto KI) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of tile t has landed in LDS
+      __builtin_amdgcn_s_barrier();         // every wave's share too; all waves are done with tile t - 1
+      if (t + 1 < ntile) load_tile(entry(t + 1) & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
+      constexpr int kbo = decltype(KI)::value * kTileBytes / 16, vbo = kbo;
+      const int e = entry(t);
+      const int kb = e & 0xffffff;
+      const int mode = slot_on ? (e >> (24 + 2 * slot)) & 3 : 0;
+      if (mode) {
+        const bool diag = kb == qb;
+        bool tile_bias = false;
+        if (qb - kb <= bias_dmax) {
+          const int base = (qb - kb) * B;
 #pragma unroll
-          for (int x = 0; x < 16; ++x) s[x] *= sl2;
-          int rr = r_in_blk - 8 * hl;  // r >= c  <=>  rr >= C
-          asm volatile("" : "+v"(rr));
-          if (tile_bias) {
+          for (int t2 = 0; t2 < 8; ++t2) tile_bias |= boff[t2] > base - B && boff[t2] < base + B;
+        }
+        const bool masked = diag || mode != kModeFull || (kb + 1) * B > dm.n;
+        const bool slow = masked || tile_bias;
+        const float ksc = slow ? 1.0f : sl2;  // multiplier from stored scores to log2 units
+
+        f32x16 S[2];       // scores of quarters a and a + 1 (by parity)
+        unsigned P[2][8];  // packed bf16 probabilities of quarters a - 1 and a (by parity), [4 s2 + j]
+        auto qk = [&](int a) {
+          f32x16 acc;
 #pragma unroll
-            for (int t2 = 0; t2 < 8; ++t2) {
-              if (boff[t2] < 0) continue;
-              const int cstar = rr - (boff[t2] - (qb - kb) * B);  // r - c == off  <=>  C == cstar
+          for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
 #pragma unroll
-              for (int x = 0; x < 16; ++x)
-                if (32 * a + 16 * (x >> 3) + (x & 7) == cstar) s[x] += bval[t2];
+          for (int kc = 0; kc < 8; ++kc)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(koff[kc][kbo + a * 32 * 16]),
+                                                          qreg[kc], acc, 0, 0, 0);
+          S[a & 1] = acc;
+        };
+        auto pv = [&](int a) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8_t Pb = as_bf16x8(make_uint4(P[a & 1][4 * s2 + 0], P[a & 1][4 * s2 + 1],
+                                                     P[a & 1][4 * s2 + 2], P[a & 1][4 * s2 + 3]));
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+              oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(voff[2 * a + s2][vbo + t2 * 32 * 16]), Pb, oacc[t2], 0, 0, 0);
+          }
+        };
+        // masks / bias and the running max of quarter a; rescales O and l when needed
+        auto soft_max = [&](int a) -> float {
+          f32x16& s = S[a & 1];
+          if (slow) {
+#pragma unroll
+            for (int x = 0; x < 16; ++x) s[x] *= sl2;
+            int rr = r_in_blk - 8 * hl;  // r >= c  <=>  rr >= C
+            asm volatile("" : "+v"(rr));
+            if (tile_bias) {
+#pragma unroll
+              for (int t2 = 0; t2 < 8; ++t2) {
+                if (boff[t2] < 0) continue;
+                const int cstar = rr - (boff[t2] - (qb - kb) * B);  // r - c == off  <=>  C == cstar
+#pragma unroll
+                for (int x = 0; x < 16; ++x)
+                  if (32 * a + 16 * (x >> 3) + (x & 7) == cstar) s[x] += bval[t2];
+              }
+            }
+            if (masked) {
+              const bool lower_ok = (mode & kModeLower) != 0;
+              const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
+              const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
+#pragma unroll
+              for (int x = 0; x < 16; ++x) {
+                const int C = 32 * a + 16 * (x >> 3) + (x & 7);
+                const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
+                if (!keep) s[x] = -__builtin_inff();
+              }
             }
           }
-          if (masked) {
-            const bool lower_ok = (mode & kModeLower) != 0;
-            const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
-            const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
+          float mx = s[0];
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-              const int C = 32 * a + 16 * (x >> 3) + (x & 7);
-              const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
-              if (!keep) s[x] = -__builtin_inff();
-            }
+          for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[x]);
+          mx *= ksc;
+          mx = half_swap_max(mx);
+          // lazy rescaling: the running max moves (and O, l are rescaled) only when
+          // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
+          if (__any(mx > m_run + 8.0f)) {
+            const float m_new = mx > m_run ? mx : m_run;
+            const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+              for (int x = 0; x < 16; ++x) oacc[t2][x] *= alpha;
           }
-        }
-        float mx = s[0];
+          return m_run == -__builtin_inff() ? 0.0f : m_run;
+        };
+        // probabilities of quarter a as packed bf16, row sums from the same bf16 values
+        auto soft_exp = [&](int a, float m_use) {
+          float psum = l_run;
 #pragma unroll
-        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[x]);
-        mx *= ksc;
-        mx = half_swap_max(mx);
-        // lazy rescaling: the running max moves (and O, l are rescaled) only when
-        // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
-        if (__any(mx > m_run + 8.0f)) {
-          const float m_new = mx > m_run ? mx : m_run;
-          const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
+          for (int x = 0; x < 16; x += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
+            P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
+            psum = sum_bf16x2(P[a & 1][x >> 1], psum);
+          }
+          l_run = psum;
 #pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) oacc[t2][x] *= alpha;
-        }
-        return m_run == -__builtin_inff() ? 0.0f : m_run;
-      };
-      // probabilities of quarter a as packed bf16, row sums from the same bf16 values
-      auto soft_exp = [&](int a, float m_use) {
-        float psum = l_run;
-#pragma unroll
-        for (int x = 0; x < 16; x += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
-          P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
-          psum = sum_bf16x2(P[a & 1][x >> 1], psum);
-        }
-        l_run = psum;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pin(P[a & 1][j]);
-      };
+          for (int j = 0; j < 8; ++j) pin(P[a & 1][j]);
+        };
 
-      qk(0);
+        qk(0);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float m_use = soft_max(a);
-        if (a < 3) qk(a + 1);
-        if (a > 0) pv(a - 1);
-        soft_exp(a, m_use);
+        for (int a = 0; a < 4; ++a) {
+          const float m_use = soft_max(a);
+          if (a < 3) qk(a + 1);
+          if (a > 0) pv(a - 1);
+          soft_exp(a, m_use);
+        }
+        pv(3);
       }
-      pv(3);
-    }
-  };
+    };
 
-  if (ntile > 0) load_tile(entry(0) & 0xffffff, std::integral_constant<int, 0>());
-  for (int t = 0; t < ntile; t += 2) {
-    tile_step(t, std::integral_constant<int, 0>());
-    if (t + 1 < ntile) tile_step(t + 1, std::integral_constant<int, 1>());
-  }
-
-  if (!slot_on || qrow >= dm.n) return;
-  const float l_tot = half_swap_sum(l_run);
-  const float inv = 1.0f / l_tot;
-  bf16_t* op = o + ((size_t)bh * dm.n + qrow) * D;
-#pragma unroll
-  for (int t2 = 0; t2 < 4; ++t2)
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const int d0 = 32 * t2 + 8 * gg + 4 * hl;
-      uint2 wv;
-      wv.x = pack_bf16x2(oacc[t2][4 * gg + 0] * inv, oacc[t2][4 * gg + 1] * inv);
-      wv.y = pack_bf16x2(oacc[t2][4 * gg + 2] * inv, oacc[t2][4 * gg + 3] * inv);
-      *reinterpret_cast<uint2*>(op + d0) = wv;
+    if (ntile > 0) load_tile(entry(0) & 0xffffff, std::integral_constant<int, 0>());
+    for (int t = 0; t < ntile; t += 2) {
+      tile_step(t, std::integral_constant<int, 0>());
+      if (t + 1 < ntile) tile_step(t + 1, std::integral_constant<int, 1>());
     }
+
+    const float l_tot = half_swap_sum(l_run);
+    if (slot_on && qrow < dm.n) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* op = o + ((size_t)bh * dm.n + qrow) * D;
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int d0 = 32 * t2 + 8 * gg + 4 * hl;
+          uint2 wv;
+          wv.x = pack_bf16x2(oacc[t2][4 * gg + 0] * inv, oacc[t2][4 * gg + 1] * inv);
+          wv.y = pack_bf16x2(oacc[t2][4 * gg + 2] * inv, oacc[t2][4 * gg + 3] * inv);
+          *reinterpret_cast<uint2*>(op + d0) = wv;
+        }
+    }
+  }  // items
 }
 
 // V^T of one KV head with keys padded to npad (a multiple of B) with zeros:
@@ -645,9 +670,13 @@ hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, in
   return hipGetLastError();
 }
 
+__global__ void zero_counters_kernel(int* counters) {
+  if (threadIdx.x < 8) counters[threadIdx.x] = 0;
+}
+
 hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q, const void* k,
                             const void* v, void* o, const int* tiles, const int* tile_cnt, const int* ulist,
-                            const int* ucnt, void* vt, hipStream_t st) {
+                            const int* ucnt, void* vt, int* counters, hipStream_t st) {
   if (use_matrix_engine(dm)) {
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
@@ -656,11 +685,20 @@ hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q,
     const int npad = dm.nb * dm.B;
     transpose_v_kernel<<<dim3(npad / 64, dm.bkv), 256, 0, st>>>(static_cast<const bf16_t*>(v), vvt, dm.n, npad);
     const int pairs = (dm.group + 1) / 2;
-    const int items = dm.bkv * pairs * dm.nb;
+    const long long combos = (long long)dm.bkv * pairs;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long long items = combos * dm.nb;
+    const int grid = (int)(items < cus ? items : cus);  // one persistent workgroup per CU
+    zero_counters_kernel<<<1, 64, 0, st>>>(counters);
     if (tiles == nullptr)
-      attn_mfma_kernel<true><<<items, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, nullptr, nullptr, pairs, npad);
+      attn_mfma_kernel<true><<<grid, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, nullptr, nullptr, pairs, npad,
+                                                    counters);
     else
-      attn_mfma_kernel<false><<<items, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, ulist, ucnt, pairs, npad);
+      attn_mfma_kernel<false><<<grid, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, ulist, ucnt, pairs, npad,
+                                                     counters);
   } else if (dm.dtype == 1) {
     if (dm.d == 128) launch_generic<bf16_t, 128>(dm, bias, q, k, v, o, tiles, tile_cnt, st);
     else launch_generic<bf16_t, 64>(dm, bias, q, k, v, o, tiles, tile_cnt, st);

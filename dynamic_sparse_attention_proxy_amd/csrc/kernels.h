@@ -79,10 +79,11 @@ bool use_matrix_engine(const Dims& dm);  // bf16, d = 128, B = 128
 // union lists of query-head pairs [bkv * pairs][ntri] + counts [bkv * pairs][nb]
 hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt, int* ulist,
                               int* ucnt, hipStream_t st);
-// tiles == nullptr: dense causal.  vt: scratch for V^T of every KV head, keys padded to
-// nb * B (bkv * d * nb * B elements), used by the matrix engine.
+// tiles == nullptr: dense causal.  Scratch used by the matrix engine: vt holds V^T of
+// every KV head with keys padded to nb * B (bkv * d * nb * B elements); counters
+// holds the 8 work-queue counters.
 hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q, const void* k,
                             const void* v, void* o, const int* tiles, const int* tile_cnt, const int* ulist,
-                            const int* ucnt, void* vt, hipStream_t st);
+                            const int* ucnt, void* vt, int* counters, hipStream_t st);
 
 }  // namespace crisp
