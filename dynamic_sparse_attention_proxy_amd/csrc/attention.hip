@@ -381,7 +381,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
           }
         };
         // masks / bias and the running max of quarter a; rescales O and l when needed
-        auto soft_max = [&](int a) -> float {
+        // masks and bias of quarter a (tiles that need them only)
+        auto soft_mask = [&](int a) {
           f32x16& s = S[a & 1];
           if (slow) {
 #pragma unroll
@@ -410,14 +411,35 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
               }
             }
           }
-          float mx = s[0];
+        };
+        // probabilities 2^(s - m_run) of quarter a as packed bf16 and their sum
+        // (from the same bf16 values)
+        auto soft_exp = [&](int a, float m_use) -> float {
+          float qsum = 0.0f;
 #pragma unroll
-          for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[x]);
-          mx *= ksc;
-          mx = half_swap_max(mx);
-          // lazy rescaling: the running max moves (and O, l are rescaled) only when
-          // some row of the wave grows by more than 2^8; else p = 2^(s - m_run) <= 256
-          if (__any(mx > m_run + 8.0f)) {
+          for (int x = 0; x < 16; x += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
+            P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
+            qsum = sum_bf16x2(P[a & 1][x >> 1], qsum);
+          }
+          return qsum;
+        };
+        // Lazy softmax: the reference m_run moves only when a quarter's probability
+        // sum leaves [0, 2^64) (or is not a number: the first quarter, where m_run is
+        // still -inf).  Then the quarter is redone against the row maximum and O and
+        // l are rescaled to it.  Every p then stays below 2^64, so O and l cannot
+        // overflow, and the result equals the one with any other reference.
+        auto soft = [&](int a) {
+          float qsum = soft_exp(a, m_run);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pin(P[a & 1][j]);
+          if (__any(__float_as_uint(qsum) >= 0x5f800000u)) {
+            const f32x16& s = S[a & 1];
+            float mx = s[0];
+#pragma unroll
+            for (int x = 1; x < 16; ++x) mx = fmaxf(mx, s[x]);
+            mx = half_swap_max(mx * ksc);
             const float m_new = mx > m_run ? mx : m_run;
             const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
@@ -426,31 +448,18 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
             for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
               for (int x = 0; x < 16; ++x) oacc[t2][x] *= alpha;
+            qsum = soft_exp(a, m_run == -__builtin_inff() ? 0.0f : m_run);
           }
-          return m_run == -__builtin_inff() ? 0.0f : m_run;
-        };
-        // probabilities of quarter a as packed bf16, row sums from the same bf16 values
-        auto soft_exp = [&](int a, float m_use) {
-          float psum = l_run;
-#pragma unroll
-          for (int x = 0; x < 16; x += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
-            P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
-            psum = sum_bf16x2(P[a & 1][x >> 1], psum);
-          }
-          l_run = psum;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pin(P[a & 1][j]);
+          l_run += qsum;
         };
 
         qk(0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const float m_use = soft_max(a);
+          soft_mask(a);
           if (a < 3) qk(a + 1);
           if (a > 0) pv(a - 1);
-          soft_exp(a, m_use);
+          soft(a);
         }
         pv(3);
       }
