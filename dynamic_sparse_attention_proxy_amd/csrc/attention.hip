@@ -359,14 +359,32 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
 
         f32x16 S[2];       // scores of quarters a and a + 1 (by parity)
         unsigned P[2][8];  // packed bf16 probabilities of quarters a - 1 and a (by parity), [4 s2 + j]
+        // operand fragments: K of the next quarter's scores is read one step ahead,
+        // V^T of the quarter whose P V product runs in this step at the step start;
+        // pinf forces a read to complete (one wait per group rather than per
+        // instruction)
+        u32x4_t kf[8], vf[8];
+        auto kload = [&](int a) {
+#pragma unroll
+          for (int kc = 0; kc < 8; ++kc) kf[kc] = koff[kc][kbo + a * 32 * 16];
+        };
+        auto vload = [&](int a) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) vf[4 * s2 + t2] = voff[2 * a + s2][vbo + t2 * 32 * 16];
+        };
+        auto pinf = [&](u32x4_t* f) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(f[j]));
+        };
         auto qk = [&](int a) {
           f32x16 acc;
 #pragma unroll
           for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
 #pragma unroll
           for (int kc = 0; kc < 8; ++kc)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(koff[kc][kbo + a * 32 * 16]),
-                                                          qreg[kc], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kc]), qreg[kc], acc, 0, 0, 0);
           S[a & 1] = acc;
         };
         auto pv = [&](int a) {
@@ -376,8 +394,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
                                                      P[a & 1][4 * s2 + 2], P[a & 1][4 * s2 + 3]));
 #pragma unroll
             for (int t2 = 0; t2 < 4; ++t2)
-              oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  as_bf16x8(voff[2 * a + s2][vbo + t2 * 32 * 16]), Pb, oacc[t2], 0, 0, 0);
+              oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[4 * s2 + t2]), Pb, oacc[t2], 0, 0, 0);
           }
         };
         // masks / bias and the running max of quarter a; rescales O and l when needed
@@ -453,14 +470,20 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
           l_run += qsum;
         };
 
+        kload(0);
         qk(0);
+        kload(1);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+          if (a > 0) vload(a - 1);
+          if (a < 3) pinf(kf);
           soft_mask(a);
           if (a < 3) qk(a + 1);
-          if (a > 0) pv(a - 1);
+          if (a < 2) kload(a + 2);
+          if (a > 0) { pinf(vf); pv(a - 1); }
           soft(a);
         }
+        vload(3);
         pv(3);
       }
     };
