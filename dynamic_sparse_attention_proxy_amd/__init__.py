@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcrisp.so")
 
 F32, BF16 = 0, 1
-SELECT_NOISE_FLOOR, SELECT_KEEP_ALL = 0, 1
+SELECT_NOISE_FLOOR, SELECT_KEEP_ALL, SELECT_CUMULATIVE = 0, 1, 2
 
 STATUS = {0: "CRISP_OK", -1: "CRISP_ERR_NULL", -2: "CRISP_ERR_SHAPE", -3: "CRISP_ERR_DTYPE",
           -4: "CRISP_ERR_CONFIG", -5: "CRISP_ERR_WORKSPACE", -6: "CRISP_ERR_CAPACITY", -7: "CRISP_ERR_HIP",

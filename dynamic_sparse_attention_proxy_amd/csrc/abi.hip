@@ -41,7 +41,8 @@ crisp_status make_dims(const crisp_shape* sh, const crisp_config* cfg, Dims* dm)
   if (cfg->w_sink < 1 || cfg->w_local < 1) return CRISP_ERR_CONFIG;
   if (cfg->tau_den == 0 || cfg->alpha_den == 0 || cfg->gamma_den == 0) return CRISP_ERR_CONFIG;
   if (cfg->gamma_num > cfg->gamma_den) return CRISP_ERR_CONFIG;
-  if (cfg->select_mode != CRISP_SELECT_NOISE_FLOOR && cfg->select_mode != CRISP_SELECT_KEEP_ALL)
+  if (cfg->select_mode != CRISP_SELECT_NOISE_FLOOR && cfg->select_mode != CRISP_SELECT_KEEP_ALL &&
+      cfg->select_mode != CRISP_SELECT_CUMULATIVE)
     return CRISP_ERR_CONFIG;
   Dims d;
   d.batch = sh->batch;
@@ -261,6 +262,7 @@ crisp_status crisp_select_indices(const crisp_shape* shape, const crisp_config* 
   sa.gamma_num = cfg->gamma_num;
   sa.gamma_den = cfg->gamma_den;
   sa.keep_all = cfg->select_mode == CRISP_SELECT_KEEP_ALL;
+  sa.cumulative = cfg->select_mode == CRISP_SELECT_CUMULATIVE;
   (void)hipGetLastError();
   if (launch_select(d, sa, q, k, ss, index_out(idx), static_cast<hipStream_t>(stream)) != hipSuccess)
     return CRISP_ERR_HIP;

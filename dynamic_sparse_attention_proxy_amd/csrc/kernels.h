@@ -29,7 +29,8 @@ struct RouteArgs {
 
 struct SelectArgs {
   unsigned alpha_num, alpha_den, gamma_num, gamma_den;
-  int keep_all;
+  int keep_all;    // every head keeps its full causal set
+  int cumulative;  // VS heads use the cumulative-coverage rule instead of Eq. 3-4
 };
 
 // Scratch regions (device pointers carved from the caller's workspace).

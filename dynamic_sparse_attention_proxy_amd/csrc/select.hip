@@ -6,6 +6,12 @@
 // alpha_den (N_b - 2) p_b > alpha_num M in exact integers, compacted into
 // ascending lists with wave ballots.
 //
+// VS heads, cumulative coverage (the FlexPrefill-style rule the pages contrast
+// with Eq. 4; selectable for comparison): per direction the shortest prefix of
+// the blocks ordered by (mass desc, index asc) whose mass reaches gamma of the
+// total, plus the first and last block; found by a radix select over the 48-bit
+// masses inside one workgroup per (head, direction).
+//
 // PE heads, GlobalAdaptive (Alg. 4): block means of Q and K (sequential fp32
 // sums), pooled scores zbar = fl(fma-chain(Qbar, Kbar) c) for kb <= qb, row
 // softmax with exp_crisp and int64 sums, quantised map Abar_q, total Tbar.
@@ -59,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void vs_select_kernel(Dims dm, SelectArgs
     if (tid < 2) io.vs_count[bh * 2 + tid] = 0;
     return;
   }
+  if (sa.cumulative) return;  // vs_cumulative_kernel
   const long long T = io.mass_total[bh];
   for (int dir = 0; dir < 2; ++dir) {
     const long long* p = (dir == 0 ? io.mass_v : io.mass_s) + (size_t)bh * nb;
@@ -88,6 +95,93 @@ __global__ __launch_bounds__(kThreads) void vs_select_kernel(Dims dm, SelectArgs
     if (tid == 0) io.vs_count[bh * 2 + dir] = cnt;
     __syncthreads();
   }
+}
+
+// Cumulative coverage for VS heads: one workgroup per (head, direction).
+constexpr int kCumThreads = 1024;
+constexpr int kCumBins = 4096;  // 12-bit digits: four passes cover the 48-bit masses
+
+__global__ __launch_bounds__(kCumThreads) void vs_cumulative_kernel(Dims dm, SelectArgs sa, IndexOut io) {
+  __shared__ unsigned int cnt[kCumBins];
+  __shared__ unsigned long long mass[kCumBins];
+  __shared__ long long part[kCumThreads];
+  __shared__ long long cut[2];  // remaining mass, value prefix
+  __shared__ int wave_cnt[kCumThreads / 64];
+  const int bh = blockIdx.x >> 1, dir = blockIdx.x & 1, tid = threadIdx.x, nb = dm.nb;
+  if (!io.route[bh]) return;  // PE head: counts written by vs_select_kernel
+  const long long* p = (dir == 0 ? io.mass_v : io.mass_s) + (size_t)bh * nb;
+  int* list = (dir == 0 ? io.vs_vertical : io.vs_slash) + (size_t)bh * nb;
+  const long long T = io.mass_total[bh];
+  // target: the smallest integer cum with gamma_den cum >= gamma_num T
+  const unsigned __int128 num = (unsigned __int128)sa.gamma_num * (unsigned __int128)T;
+  const long long tgt = (long long)((num + sa.gamma_den - 1) / sa.gamma_den);
+  constexpr long long kNone = 0x7fffffffffffffffLL;
+  long long vstar = kNone, rties = 0;  // cut value and the number of ties at it to take
+  if (tgt > 0 && nb > 2) {
+    long long R = tgt, prefix = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 36 - 12 * pass;
+      for (int i = tid; i < kCumBins; i += kCumThreads) cnt[i] = 0, mass[i] = 0;
+      __syncthreads();
+      for (int b = tid; b < nb; b += kCumThreads) {
+        const long long v = p[b];
+        if ((v >> (shift + 12)) == (prefix >> (shift + 12))) {
+          const int dg = (int)((v >> shift) & (kCumBins - 1));
+          atomicAdd(&cnt[dg], 1u);
+          atomicAdd(&mass[dg], (unsigned long long)v);
+        }
+      }
+      __syncthreads();
+      // thread t owns digits 4095 - 4t .. 4095 - 4t - 3 (largest first)
+      long long mine = 0;
+      for (int k2 = 0; k2 < 4; ++k2) mine += (long long)mass[kCumBins - 1 - (4 * tid + k2)];
+      part[tid] = mine;
+      __syncthreads();
+      for (int off = 1; off < kCumThreads; off <<= 1) {
+        const long long v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+      }
+      const long long before = part[tid] - mine;
+      if (before < R && R <= before + mine) {  // the digit where the running mass reaches R
+        long long c = before;
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int dg = kCumBins - 1 - (4 * tid + k2);
+          const long long m = (long long)mass[dg];
+          if (c + m >= R) {
+            cut[0] = R - c;
+            cut[1] = prefix | ((long long)dg << shift);
+            break;
+          }
+          c += m;
+        }
+      }
+      __syncthreads();
+      R = cut[0];
+      prefix = cut[1];
+      __syncthreads();
+    }
+    vstar = prefix;                  // > 0: the remaining mass R > 0 lies in this value
+    rties = (R + vstar - 1) / vstar;  // ties at v* needed, lowest indices first
+  }
+  int cnt_out = 0;
+  long long tcur = 0;
+  for (int base = 0; base < nb; base += kCumThreads) {
+    const int b = base + tid;
+    const bool in = b < nb;
+    const long long v = in ? p[b] : 0;
+    const bool tie = in && v == vstar;
+    int ntie;
+    const int tpos = block_compact(tie, wave_cnt, &ntie);
+    const bool flag = in && (nb <= 2 || b == 0 || b == nb - 1 || v > vstar || (tie && tcur + tpos < rties));
+    tcur += ntie;
+    int tot;
+    const int pos = block_compact(flag, wave_cnt, &tot);
+    if (flag) list[cnt_out + pos] = b;
+    cnt_out += tot;
+  }
+  if (tid == 0) io.vs_count[bh * 2 + dir] = cnt_out;
 }
 
 // ------------------------------------------------------------- PE path ----
@@ -496,6 +590,7 @@ void launch_pool(const Dims& dm, const void* q, const void* k, const IndexOut& i
 hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, const void* k,
                          const SelectScratch& ws, const IndexOut& io, hipStream_t st) {
   vs_select_kernel<<<dm.bh, kThreads, 0, st>>>(dm, sa, io);
+  if (sa.cumulative) vs_cumulative_kernel<<<dm.bh * 2, kCumThreads, 0, st>>>(dm, sa, io);
   if (!sa.keep_all) {
     if (dm.dtype == 1)
       launch_pool<bf16_t>(dm, q, k, io, ws.qbar, ws.kbar, st);

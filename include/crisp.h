@@ -69,7 +69,11 @@ typedef enum { CRISP_F32 = 0, CRISP_BF16 = 1 } crisp_dtype;
 
 typedef enum {
   CRISP_SELECT_NOISE_FLOOR = 0, /* the method: Eq. 3-4 for VS heads, Alg. 4 for PE heads */
-  CRISP_SELECT_KEEP_ALL = 1     /* every head keeps its complete causal index set (dense check) */
+  CRISP_SELECT_KEEP_ALL = 1,    /* every head keeps its complete causal index set (dense check) */
+  CRISP_SELECT_CUMULATIVE = 2   /* comparison: VS heads keep, per direction, the shortest prefix of
+                                   blocks by (mass desc, index asc) covering gamma of the total mass,
+                                   plus the first and last block (the cumulative-coverage rule the
+                                   summary page's Introduction contrasts with Eq. 4); PE as mode 0 */
 } crisp_select_mode;
 
 typedef struct {

@@ -176,12 +176,14 @@ def pe_index(qh, kh, B, gamma=(19, 20), want_abar=False, threads=0):
 
 
 def index_sets(q, k, B, w_sink, w_local, tau=(1, 10), alpha=(1, 1), gamma=(19, 20),
-               bias_offsets=None, bias_values=None, keep_all=False):
+               bias_offsets=None, bias_values=None, keep_all=False, cumulative=False):
     """Alg. 1 up to the sparse attention: route every head, then its index set.
 
     Returns dict(proxy=<proxy dict>, heads=[...]) with one entry per query head:
     {"route": 1, "vertical": ids, "slash": ids} or {"route": 0, "rowptr", "cols"}.
     keep_all: every head keeps its complete (causal) index set.
+    cumulative: VS heads use the cumulative-coverage rule (cumulative_select with
+    gamma) instead of the noise floor; PE heads are unchanged.
     """
     pr = proxy(q, k, B, w_sink, w_local, tau, bias_offsets, bias_values)
     bh = q.shape[0]
@@ -203,6 +205,9 @@ def index_sets(q, k, B, w_sink, w_local, tau=(1, 10), alpha=(1, 1), gamma=(19, 2
             if keep_all:
                 vv = np.arange(nb, dtype=np.int32)
                 ss = np.arange(nb, dtype=np.int32)
+            elif cumulative:
+                vv = cumulative_select(pr["mass_v"][h], pr["total"][h], gamma)
+                ss = cumulative_select(pr["mass_s"][h], pr["total"][h], gamma)
             else:
                 vv = vs_select(pr["mass_v"][h], pr["total"][h], alpha)
                 ss = vs_select(pr["mass_s"][h], pr["total"][h], alpha)

@@ -98,6 +98,13 @@ def test_null_alignment_workspace_capacity(lib):
     assert lib.crisp_dense_prefill(sh, cf, fake, fake, fake, None, None, ws, fake, None) == -1
 
 
+def test_select_modes(lib):
+    """Noise floor, keep-all and the cumulative comparison mode validate; others do not."""
+    for mode in (crisp.SELECT_NOISE_FLOOR, crisp.SELECT_KEEP_ALL, crisp.SELECT_CUMULATIVE):
+        assert crisp.workspace_size(_spec(select_mode=mode)) > 0
+    assert crisp.workspace_size(_spec(select_mode=3)) == 0
+
+
 def test_status_strings(lib):
     for code in range(-8, 1):
         assert lib.crisp_status_string(code)

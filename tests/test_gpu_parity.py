@@ -41,7 +41,8 @@ def _case(name, wl=None, select_mode=crisp.SELECT_NOISE_FLOOR):
     with Timer(f"oracle index sets {name}"):
         ref = oracle.index_sets(I.q, I.k, wl.block, wl.w_sink, wl.w_local, synth.TAU, synth.ALPHA, synth.GAMMA,
                                 I.bias_offsets, I.bias_values,
-                                keep_all=select_mode == crisp.SELECT_KEEP_ALL)
+                                keep_all=select_mode == crisp.SELECT_KEEP_ALL,
+                                cumulative=select_mode == crisp.SELECT_CUMULATIVE)
     _cache[key] = (wl, I, X, spec, bufs, ref)
     return _cache[key]
 
@@ -105,6 +106,19 @@ def test_keep_all_equals_dense(name):
     o_de = run_dense(spec, X)
     import torch
     assert torch.equal(o_sp, o_de)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny", "llama_32k", "qwen_128k"])
+def test_cumulative_mode(name):
+    """The cumulative-coverage comparison mode: VS lists bit-exact against the oracle's
+    cumulative rule on the same masses, attention within tolerance."""
+    wl, I, X, spec, bufs, ref = _case(name, select_mode=crisp.SELECT_CUMULATIVE)
+    gpu = download_index_sets(bufs)
+    bad = compare_index_sets(gpu, ref)
+    assert not bad, "\n".join(bad[:20])
+    rows = None if name == "tiny" else synth.sample_rows(wl)
+    _check_attention(wl, I, X, spec, bufs, ref, rows, f"{name} cumulative")
 
 
 @pytest.mark.timeout(600)
