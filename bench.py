@@ -131,6 +131,55 @@ def cpu_baseline(wl, I, seconds_hint=20.0):
                          "attention": round(t_att * 1e3, 1)}}
 
 
+def selection_sweep(names=("llama_32k", "llama_128k", "llama_512k")):
+    """Selected budget and sparse-attention time of the noise-floor rule against the
+    cumulative-coverage rule, over sequence length (VS heads; PE heads are the same)."""
+    import numpy as np
+    import torch
+
+    import dynamic_sparse_attention_proxy_amd as crisp
+    import synth
+    out = {}
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        I = synth.make_inputs(wl)
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        q = torch.from_numpy(I.q).cuda().to(dt)
+        k = torch.from_numpy(I.k).cuda().to(dt)
+        v = torch.from_numpy(I.v).cuda().to(dt)
+        bo = torch.from_numpy(I.bias_offsets).cuda()
+        bv = torch.from_numpy(I.bias_values).cuda()
+        del I
+        row = {}
+        for mode, label in ((crisp.SELECT_NOISE_FLOOR, "noise_floor"), (crisp.SELECT_CUMULATIVE, "cumulative")):
+            spec = crisp.LayerSpec(batch=wl.batch, n_q_heads=wl.hq, n_kv_heads=wl.hkv, seq_len=wl.n, head_dim=wl.d,
+                                   dtype=crisp.BF16 if wl.dtype == "bf16" else crisp.F32, block=wl.block,
+                                   w_sink=wl.w_sink, w_local=wl.w_local, tau=synth.TAU, alpha=synth.ALPHA,
+                                   gamma=synth.GAMMA, select_mode=mode)
+            bufs = crisp.Buffers(spec)
+            o = torch.empty_like(q)
+            crisp.route(spec, q, k, bufs, bo, bv)
+            crisp.select_indices(spec, q, k, bufs)
+            crisp.sparse_prefill(spec, q, k, v, o, bufs, bo, bv)
+            stream = torch.cuda.current_stream()
+            ms = min(time_calls(lambda: crisp.sparse_prefill(spec, q, k, v, o, bufs, bo, bv), 2, stream))
+            vs = bufs.route.cpu().numpy().astype(bool)
+            cnt = bufs.vs_count.cpu().numpy()[vs]
+            tiles = np.array(tile_counts(bufs, spec))[vs]
+            nb = spec.num_blocks
+            row[label] = {"vertical_blocks": round(float(cnt[:, 0].mean()), 1),
+                          "slash_blocks": round(float(cnt[:, 1].mean()), 1),
+                          "vs_tile_density": round(float(tiles.mean()) / (nb * (nb + 1) / 2), 4),
+                          "attention_ms": round(ms, 2)}
+            del bufs, o
+            torch.cuda.empty_cache()
+        out[name] = row
+        log(f"sweep {name}: {row}")
+        del q, k, v
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(gib: float = 4.0):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -228,6 +277,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K speedup side measurement")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--selection-sweep", action="store_true",
+                    help="add the noise-floor vs cumulative-coverage budget over 32K/128K/512K")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -294,6 +345,8 @@ def main():
                           "speedup_vs_dense": round(r2["dense_ms"] / tot2, 3),
                           "stage_ms": {kk: round(vv, 3) for kk, vv in st2.items()}}
         del r2
+    if args.selection_sweep:
+        out["selection_sweep"] = selection_sweep()
     if not args.no_cpu_baseline:
         t = time.time()
         out["cpu_baseline"] = cpu_baseline(wl, r["I"])
