@@ -100,17 +100,18 @@ Layout layout(const Dims& d) {
   L.s_end = o;
 
   o = 0;
-  L.a_tiles = o;
-  o = align_up(o + (size_t)d.bh * d.ntri * sizeof(int));
-  L.a_cnt = o;
-  o = align_up(o + (size_t)d.bh * d.nb * sizeof(int));
+  const bool mat = use_matrix_engine(d);
   const size_t pairs = (size_t)d.bkv * ((d.group + 1) / 2);
-  L.a_ulist = o;
-  o = align_up(o + pairs * d.ntri * sizeof(int));
+  L.a_tiles = o;  // per-head lists (vector engine)
+  if (!mat) o = align_up(o + (size_t)d.bh * d.ntri * sizeof(int));
+  L.a_cnt = o;
+  if (!mat) o = align_up(o + (size_t)d.bh * d.nb * sizeof(int));
+  L.a_ulist = o;  // pair lists (matrix engine)
+  if (mat) o = align_up(o + pairs * d.ntri * sizeof(int));
   L.a_ucnt = o;
-  o = align_up(o + pairs * d.nb * sizeof(int));
+  if (mat) o = align_up(o + pairs * d.nb * sizeof(int));
   L.a_vt = o;
-  if (use_matrix_engine(d)) o = align_up(o + (size_t)d.bkv * d.d * d.nb * d.B * 2);  // V^T, bf16
+  if (mat) o = align_up(o + (size_t)d.bkv * d.d * d.nb * d.B * 2);  // V^T, bf16
   L.a_qcnt = o;
   o = align_up(o + 8 * sizeof(int));  // work-queue counters
   L.a_end = o;

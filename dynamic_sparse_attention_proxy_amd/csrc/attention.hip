@@ -546,42 +546,64 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restri
   }
 }
 
-// Union of the tile lists of the two query heads of a pair (same KV head,
-// same query block): ascending kb, with each head's mask mode (0 = absent).
-__global__ void union_tiles_kernel(Dims dm, int pairs, const int* __restrict__ tiles,
-                                   const int* __restrict__ tile_cnt, int* __restrict__ ulist,
-                                   int* __restrict__ ucnt) {
-  const int qb = blockIdx.x * blockDim.x + threadIdx.x;
-  const int item = blockIdx.y;
-  if (qb >= dm.nb) return;
+// Tile list of a work item of the matrix engine (KV head g, query-head pair w,
+// query block qb): ascending kb with each head's mask mode (bits 24-25 for the
+// first head of the pair, 26-27 for the second; 0 = not in that head's set).
+// One workgroup per (item, qb) marks the modes of key blocks in LDS, 4096 at a
+// time, from the heads' index sets, then compacts them in order.
+__global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, IndexOut io, int* __restrict__ ulist,
+                                                         int* __restrict__ ucnt) {
+  constexpr int kChunk = 4096;
+  __shared__ unsigned int modes[kChunk / 4];  // one byte per key block: bits 0-1 first head, 2-3 second
+  __shared__ int wave_cnt[4];
+  const int qb = blockIdx.x, item = blockIdx.y, tid = threadIdx.x;
   const int g = item / pairs, w = item % pairs;
   const int bidx = g / dm.hkv, gh = g % dm.hkv;
-  const size_t tri = (size_t)qb * (qb + 1) / 2;
-  int na = 0, nbb = 0;
-  const int* la = nullptr;
-  const int* lb = nullptr;
-  if (2 * w < dm.group) {
-    const int bh = bidx * dm.hq + gh * dm.group + 2 * w;
-    la = tiles + (size_t)bh * dm.ntri + tri;
-    na = tile_cnt[(size_t)bh * dm.nb + qb];
+  int* out = ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
+  int cnt = 0;
+  for (int c0 = 0; c0 <= qb; c0 += kChunk) {
+    const int c1 = min(c0 + kChunk, qb + 1);
+    for (int i = tid; i < kChunk / 4; i += 256) modes[i] = 0;
+    __syncthreads();
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int hin = 2 * w + s2;
+      if (hin >= dm.group) continue;
+      const int bh = bidx * dm.hq + gh * dm.group + hin;
+      auto mark = [&](int kb, int mode) {
+        if (kb >= c0 && kb < c1) {
+          if (kb == qb) mode &= kModeLower;  // diagonal tile: causal part only
+          if (mode) atomicOr(&modes[(kb - c0) >> 2], (unsigned)mode << (8 * ((kb - c0) & 3) + 2 * s2));
+        }
+      };
+      if (io.route[bh]) {
+        // vertical block kb: whole tile; slash block s: lower triangle of tile qb - s
+        // and upper triangle of tile qb - s - 1
+        const int nv = io.vs_count[bh * 2], ns = io.vs_count[bh * 2 + 1];
+        const int* V = io.vs_vertical + (size_t)bh * dm.nb;
+        const int* S = io.vs_slash + (size_t)bh * dm.nb;
+        for (int i = tid; i < nv; i += 256) mark(V[i], kModeFull);
+        for (int i = tid; i < ns; i += 256) {
+          mark(qb - S[i], kModeLower);
+          mark(qb - S[i] - 1, kModeUpper);
+        }
+      } else {
+        const int* rp = io.pe_rowptr + (size_t)bh * (dm.nb + 1);
+        const int* col = io.pe_col + (size_t)bh * io.pe_cap;
+        for (int p = rp[qb] + tid; p < rp[qb + 1]; p += 256) mark(col[p], kModeFull);
+      }
+    }
+    __syncthreads();
+    for (int base = c0; base < c1; base += 256) {
+      const int kb = base + tid;
+      const unsigned m = kb < c1 ? (modes[(kb - c0) >> 2] >> (8 * ((kb - c0) & 3))) & 15u : 0u;
+      int tot;
+      const int pos = block_compact(m != 0, wave_cnt, &tot);
+      if (m) out[cnt + pos] = kb | (int)((m & 3u) << 24) | (int)((m >> 2) << 26);
+      cnt += tot;
+    }
+    __syncthreads();
   }
-  if (2 * w + 1 < dm.group) {
-    const int bh = bidx * dm.hq + gh * dm.group + 2 * w + 1;
-    lb = tiles + (size_t)bh * dm.ntri + tri;
-    nbb = tile_cnt[(size_t)bh * dm.nb + qb];
-  }
-  int* out = ulist + (size_t)item * dm.ntri + tri;
-  int ia = 0, ib = 0, cnt = 0;
-  while (ia < na || ib < nbb) {
-    const int ka = ia < na ? (la[ia] & 0x0fffffff) : 0x7fffffff;
-    const int kbb = ib < nbb ? (lb[ib] & 0x0fffffff) : 0x7fffffff;
-    const int kk = ka < kbb ? ka : kbb;
-    int e = kk;
-    if (ka == kk) e |= (la[ia++] >> 28) << 24;
-    if (kbb == kk) e |= (lb[ib++] >> 28) << 26;
-    out[cnt++] = e;
-  }
-  ucnt[(size_t)item * dm.nb + qb] = cnt;
+  if (tid == 0) ucnt[(size_t)item * dm.nb + qb] = cnt;
 }
 
 // ----------------------------------------------------------- vector engine --
@@ -693,11 +715,11 @@ bool use_matrix_engine(const Dims& dm) { return dm.dtype == 1 && dm.d == 128 && 
 
 hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt, int* ulist,
                               int* ucnt, hipStream_t st) {
-  build_tiles_kernel<<<dim3((dm.nb + 127) / 128, dm.bh), 128, 0, st>>>(dm, io, tiles, tile_cnt);
   if (use_matrix_engine(dm)) {
     const int pairs = (dm.group + 1) / 2;
-    union_tiles_kernel<<<dim3((dm.nb + 127) / 128, dm.bkv * pairs), 128, 0, st>>>(dm, pairs, tiles, tile_cnt,
-                                                                                 ulist, ucnt);
+    pair_tiles_kernel<<<dim3(dm.nb, dm.bkv * pairs), 256, 0, st>>>(dm, pairs, io, ulist, ucnt);
+  } else {
+    build_tiles_kernel<<<dim3((dm.nb + 127) / 128, dm.bh), 128, 0, st>>>(dm, io, tiles, tile_cnt);
   }
   return hipGetLastError();
 }

@@ -76,8 +76,9 @@ hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, co
                          const SelectScratch& ws, const IndexOut& io, hipStream_t st);
 // attention.hip
 bool use_matrix_engine(const Dims& dm);  // bf16, d = 128, B = 128
-// per-head tile lists [bh][ntri] + counts [bh][nb]; for the matrix engine also the
-// union lists of query-head pairs [bkv * pairs][ntri] + counts [bkv * pairs][nb]
+// tile lists: for the matrix engine the lists of query-head pairs [bkv * pairs][ntri]
+// + counts [bkv * pairs][nb] (ulist / ucnt), else per-head lists [bh][ntri] + counts
+// [bh][nb] (tiles / tile_cnt)
 hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt, int* ulist,
                               int* ucnt, hipStream_t st);
 // tiles == nullptr: dense causal.  Scratch used by the matrix engine: vt holds V^T of

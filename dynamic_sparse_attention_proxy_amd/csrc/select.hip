@@ -40,24 +40,6 @@ __device__ __forceinline__ long long block_sum_i64(long long v, long long* red) 
   return s;
 }
 
-// Ascending compaction of flags over one block of threads.  Returns the
-// position of this thread's element (valid if flag) and the block total.
-__device__ __forceinline__ int block_compact(bool flag, int* wave_cnt, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const unsigned long long mask = __ballot(flag);
-  const int before = __popcll(mask & ((1ull << lane) - 1ull));
-  __syncthreads();
-  if (lane == 0) wave_cnt[wave] = __popcll(mask);
-  __syncthreads();
-  int off = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wave) off += wave_cnt[w];
-    tot += wave_cnt[w];
-  }
-  *total = tot;
-  return off + before;
-}
-
 __global__ __launch_bounds__(kThreads) void vs_select_kernel(Dims dm, SelectArgs sa, IndexOut io) {
   __shared__ int wave_cnt[4];
   const int bh = blockIdx.x, tid = threadIdx.x, nb = dm.nb;

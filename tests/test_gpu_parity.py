@@ -122,6 +122,27 @@ def test_cumulative_mode(name):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("alpha", [(5, 4), (3, 2)])
+def test_alpha_variants(alpha):
+    """Eq. 4 with the pages' larger multipliers: VS lists bit-exact against the oracle on the
+    same (bit-exact) masses; a larger alpha never keeps more blocks."""
+    import dataclasses
+    wl, I, X, spec, bufs, ref = _case("llama_32k")
+    spec_a = dataclasses.replace(spec, alpha=alpha)
+    b2 = run_route_select(spec_a, X)
+    gpu = download_index_sets(b2)
+    base = download_index_sets(bufs)
+    pr = ref["proxy"]
+    for h in range(wl.hq):
+        if not pr["route"][h]:
+            continue
+        for key, mk in (("vertical", "mass_v"), ("slash", "mass_s")):
+            want = oracle.vs_select(pr[mk][h], pr["total"][h], alpha)
+            assert np.array_equal(gpu["heads"][h][key], want), (h, key)
+            assert set(want.tolist()) <= set(base["heads"][h][key].tolist()), (h, key)
+
+
+@pytest.mark.timeout(600)
 def test_determinism():
     wl, I, X, spec, bufs, ref = _case("llama_32k")
     import torch
