@@ -131,10 +131,67 @@ def cpu_baseline(wl, I, seconds_hint=20.0):
                          "attention": round(t_att * 1e3, 1)}}
 
 
+def _device_layer(wl):
+    import torch
+
+    import synth
+    I = synth.make_inputs(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    X = dict(q=torch.from_numpy(I.q).cuda().to(dt), k=torch.from_numpy(I.k).cuda().to(dt),
+             v=torch.from_numpy(I.v).cuda().to(dt), bo=torch.from_numpy(I.bias_offsets).cuda(),
+             bv=torch.from_numpy(I.bias_values).cuda())
+    del I
+    return X
+
+
+def _variant_stats(wl, X, **overrides):
+    """Index-set sizes and timings of one hyper-parameter / selection-mode variant."""
+    import numpy as np
+    import torch
+
+    import dynamic_sparse_attention_proxy_amd as crisp
+    import synth
+    kw = dict(batch=wl.batch, n_q_heads=wl.hq, n_kv_heads=wl.hkv, seq_len=wl.n, head_dim=wl.d,
+              dtype=crisp.BF16 if wl.dtype == "bf16" else crisp.F32, block=wl.block, w_sink=wl.w_sink,
+              w_local=wl.w_local, tau=synth.TAU, alpha=synth.ALPHA, gamma=synth.GAMMA)
+    kw.update(overrides)
+    spec = crisp.LayerSpec(**kw)
+    q, k, v, bo, bv = X["q"], X["k"], X["v"], X["bo"], X["bv"]
+    bufs = crisp.Buffers(spec)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def index():
+        crisp.route(spec, q, k, bufs, bo, bv)
+        crisp.select_indices(spec, q, k, bufs)
+
+    def attend():
+        crisp.sparse_prefill(spec, q, k, v, o, bufs, bo, bv)
+
+    index()
+    attend()
+    t_index = min(time_calls(index, 2, stream))
+    t_att = min(time_calls(attend, 2, stream))
+    vs = bufs.route.cpu().numpy().astype(bool)
+    cnt = bufs.vs_count.cpu().numpy()
+    tiles = np.array(tile_counts(bufs, spec))
+    nb = spec.num_blocks
+    causal = nb * (nb + 1) / 2
+    row = {"vertical_blocks": round(float(cnt[vs, 0].mean()), 1) if vs.any() else None,
+           "slash_blocks": round(float(cnt[vs, 1].mean()), 1) if vs.any() else None,
+           "vs_tile_density": round(float(tiles[vs].mean()) / causal, 4) if vs.any() else None,
+           "pe_tile_density": round(float(tiles[~vs].mean()) / causal, 4) if (~vs).any() else None,
+           "tile_density": round(float(tiles.mean()) / causal, 4),
+           "route_select_ms": round(t_index, 2), "attention_ms": round(t_att, 2),
+           "total_ms": round(t_index + t_att, 2)}
+    del bufs, o
+    torch.cuda.empty_cache()
+    return row
+
+
 def selection_sweep(names=("llama_32k", "llama_128k", "llama_512k")):
     """Selected budget and sparse-attention time of the noise-floor rule against the
     cumulative-coverage rule, over sequence length (VS heads; PE heads are the same)."""
-    import numpy as np
     import torch
 
     import dynamic_sparse_attention_proxy_amd as crisp
@@ -142,40 +199,33 @@ def selection_sweep(names=("llama_32k", "llama_128k", "llama_512k")):
     out = {}
     for name in names:
         wl = synth.WORKLOADS[name]
-        I = synth.make_inputs(wl)
-        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        q = torch.from_numpy(I.q).cuda().to(dt)
-        k = torch.from_numpy(I.k).cuda().to(dt)
-        v = torch.from_numpy(I.v).cuda().to(dt)
-        bo = torch.from_numpy(I.bias_offsets).cuda()
-        bv = torch.from_numpy(I.bias_values).cuda()
-        del I
+        X = _device_layer(wl)
         row = {}
         for mode, label in ((crisp.SELECT_NOISE_FLOOR, "noise_floor"), (crisp.SELECT_CUMULATIVE, "cumulative")):
-            spec = crisp.LayerSpec(batch=wl.batch, n_q_heads=wl.hq, n_kv_heads=wl.hkv, seq_len=wl.n, head_dim=wl.d,
-                                   dtype=crisp.BF16 if wl.dtype == "bf16" else crisp.F32, block=wl.block,
-                                   w_sink=wl.w_sink, w_local=wl.w_local, tau=synth.TAU, alpha=synth.ALPHA,
-                                   gamma=synth.GAMMA, select_mode=mode)
-            bufs = crisp.Buffers(spec)
-            o = torch.empty_like(q)
-            crisp.route(spec, q, k, bufs, bo, bv)
-            crisp.select_indices(spec, q, k, bufs)
-            crisp.sparse_prefill(spec, q, k, v, o, bufs, bo, bv)
-            stream = torch.cuda.current_stream()
-            ms = min(time_calls(lambda: crisp.sparse_prefill(spec, q, k, v, o, bufs, bo, bv), 2, stream))
-            vs = bufs.route.cpu().numpy().astype(bool)
-            cnt = bufs.vs_count.cpu().numpy()[vs]
-            tiles = np.array(tile_counts(bufs, spec))[vs]
-            nb = spec.num_blocks
-            row[label] = {"vertical_blocks": round(float(cnt[:, 0].mean()), 1),
-                          "slash_blocks": round(float(cnt[:, 1].mean()), 1),
-                          "vs_tile_density": round(float(tiles.mean()) / (nb * (nb + 1) / 2), 4),
-                          "attention_ms": round(ms, 2)}
-            del bufs, o
-            torch.cuda.empty_cache()
+            row[label] = _variant_stats(wl, X, select_mode=mode)
         out[name] = row
         log(f"sweep {name}: {row}")
-        del q, k, v
+        del X
+        torch.cuda.empty_cache()
+    return out
+
+
+def param_sweep(names=("llama_128k", "llama_512k")):
+    """The pages' other hyper-parameters: the noise-floor multiplier alpha (Eq. 4) at 1, 5/4
+    and 3/2, and the pooled-estimation coverage gamma at 19/20 and 97/100."""
+    import torch
+
+    import synth
+    variants = (("alpha=1/1,gamma=19/20", {}), ("alpha=5/4", {"alpha": (5, 4)}), ("alpha=3/2", {"alpha": (3, 2)}),
+                ("gamma=97/100", {"gamma": (97, 100)}))
+    out = {}
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        X = _device_layer(wl)
+        row = {label: _variant_stats(wl, X, **ov) for label, ov in variants}
+        out[name] = row
+        log(f"param sweep {name}: {row}")
+        del X
         torch.cuda.empty_cache()
     return out
 
@@ -279,6 +329,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--selection-sweep", action="store_true",
                     help="add the noise-floor vs cumulative-coverage budget over 32K/128K/512K")
+    ap.add_argument("--param-sweep", action="store_true",
+                    help="add the alpha in {1, 5/4, 3/2} and gamma in {19/20, 97/100} variants at 128K/512K")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -347,6 +399,8 @@ def main():
         del r2
     if args.selection_sweep:
         out["selection_sweep"] = selection_sweep()
+    if args.param_sweep:
+        out["param_sweep"] = param_sweep()
     if not args.no_cpu_baseline:
         t = time.time()
         out["cpu_baseline"] = cpu_baseline(wl, r["I"])

@@ -67,6 +67,14 @@ def _load():
         lib.oracle_pe_index.restype = i64
         lib.oracle_attention_row.argtypes = [i64, i32, P, P, P, i32, P, P, P, P]
         lib.oracle_attention_row.restype = None
+        lib.oracle_log_crisp.argtypes = [ctypes.c_double]
+        lib.oracle_log_crisp.restype = ctypes.c_double
+        lib.oracle_log_crisp_array.argtypes = [P, P, i64]
+        lib.oracle_log_crisp_array.restype = None
+        lib.oracle_jsd_fixed.argtypes = [i64, P, i64, P, i64]
+        lib.oracle_jsd_fixed.restype = i64
+        lib.oracle_pooled_last_row.argtypes = [i64, i32, i32, P, P, P]
+        lib.oracle_pooled_last_row.restype = i64
         _lib = lib
     return _lib
 
@@ -220,6 +228,58 @@ def index_sets(q, k, B, w_sink, w_local, tau=(1, 10), alpha=(1, 1), gamma=(19, 2
                 rowptr, cols = pe_out[h]
             heads.append(dict(route=0, rowptr=rowptr, cols=cols))
     return dict(proxy=pr, heads=heads)
+
+
+# ------------------------------------------------------ divergence router ---
+JSD_SHIFT = 52  # per-block divergence terms are summed as rne(t 2^52); JSD = J 2^-53
+
+
+def log_crisp(x) -> np.ndarray:
+    """Natural logarithm (fp64) by 2^e m reduction and the atanh series."""
+    lib = _load()
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    lib.oracle_log_crisp_array(_p(x), _p(y), x.size)
+    return y
+
+
+def jsd_fixed(p, tp, a, ta) -> int:
+    """J = sum_b rne(t_b 2^52) of the Jensen-Shannon divergence of p / tp and a / ta."""
+    p = _c(p, np.int64)
+    a = _c(a, np.int64)
+    assert p.shape == a.shape
+    return int(_load().oracle_jsd_fixed(p.shape[0], _p(p), int(tp), _p(a), int(ta)))
+
+
+def pooled_last_row(qh, kh, B):
+    """The pooled (pool-then-softmax) estimate of one head's last query block over
+    key blocks, in the fixed point of Alg. 4.  Returns (abar [N_b] int64, total)."""
+    qh = _c(qh, np.float32)
+    kh = _c(kh, np.float32)
+    n, d = kh.shape
+    assert qh.shape == (n, d)
+    abar = np.zeros(num_blocks(n, B), np.int64)
+    t = _load().oracle_pooled_last_row(n, d, B, _p(qh), _p(kh), _p(abar))
+    return abar, int(t)
+
+
+def jsd_route(q, k, B, pr, tau_jsd=(1, 100)):
+    """The divergence router on the same proxy: per query head the pooled estimate,
+    its divergence from the per-query estimate p^v / T of the proxy dict pr, and
+    the routing decision (1 = VS iff tau_den J >= tau_num 2^53)."""
+    bh = q.shape[0]
+    G = bh // k.shape[0]
+    nb = pr["nb"]
+    out = dict(jsd=np.zeros(bh, np.int64), route=np.zeros(bh, np.uint8), abar=np.zeros((bh, nb), np.int64),
+               abar_total=np.zeros(bh, np.int64))
+    for h in range(bh):
+        abar, ta = pooled_last_row(q[h], k[h // G], B)
+        J = jsd_fixed(pr["mass_v"][h], pr["total"][h], abar, ta)
+        out["abar"][h] = abar
+        out["abar_total"][h] = ta
+        out["jsd"][h] = J
+        out["route"][h] = 1 if tau_jsd[1] * J >= tau_jsd[0] * (1 << (JSD_SHIFT + 1)) else 0
+    return out
 
 
 # ------------------------------------------------------------ attention ----

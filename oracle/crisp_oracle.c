@@ -16,6 +16,8 @@
  *            first and last blocks always kept.
  *   Alg. 4   pooled Q and K, softmax of the pooled scores, flatten, normalise,
  *            sort, keep the gamma-cumsum prefix.
+ *   Motivation / Key Contributions: the Jensen-Shannon divergence router that
+ *            C_struct replaces (pooled estimate against per-query estimate).
  *
  * Precision (the pages leave it open; these readings are stated in the design doc):
  *   - proxy scores are fp32: acc = fmaf(q[k], key[k], acc) for k ascending,
@@ -353,6 +355,133 @@ int64_t oracle_pe_index(int64_t n, int32_t d, int32_t B, const float* Qh, const 
   free(Qb);
   free(Kb);
   return nnz;
+}
+
+/* ------------------------------------------------- divergence router ---- */
+/* The router CRISP replaces (summary page, Motivation and Key Contributions):
+ * a second, pooled estimate of the head's attention, compared with the
+ * per-query one by the Jensen-Shannon divergence; the head goes to VS when
+ * the divergence reaches a threshold.  Readings (the pages give no formula):
+ *   - per-query estimate P: the proxy map of the last query block, softmax
+ *     per query first, then pooled over key blocks and queries, i.e. the
+ *     column block masses p^v_b / T of Alg. 3 (already exact int64 sums);
+ *   - pooled estimate Q: pool first, then one softmax: the block mean of the
+ *     last query block's rows against the block means of all key blocks,
+ *     z_b = fl(fma-chain(Qbar, Kbar_b) c), softmax in the same fixed point as
+ *     Alg. 4 (it is the last row of Alg. 4's pooled map);
+ *   - JSD(P, Q) = (KL(P || M) + KL(Q || M)) / 2 with M = (P + Q) / 2, natural
+ *     logarithm; route to VS iff JSD >= tau_jsd (exact rational test).
+ * Arithmetic (fixed so that a GPU can reproduce every bit): P_b and Q_b in
+ * fp64 by correctly rounded division of the int64 sums; per block
+ * t_b = fl(fl(P log_crisp(P / M)) + fl(Q log_crisp(Q / M))) with a zero term
+ * for a zero probability; J = sum_b rne(t_b 2^52) in int64, so
+ * JSD = J 2^-53 and the sum is order-free. */
+
+/* Natural logarithm in fp64 for positive normal x, after the classic
+ * reduction x = 2^e m with m in (sqrt(1/2), sqrt(2)], then
+ * ln m = 2 atanh(s), s = (m - 1) / (m + 1), by the odd series
+ * 2 (s + s^3/3 + ... + s^23/23) in Horner form in s^2 (|s| <= 0.1716, so the
+ * first omitted term is below 2^-60 relative), and
+ * ln x = e ln2 + ln m with ln2 split into a 32-bit head and a tail.  Within
+ * 3 ulp of the exact logarithm (tests measure it against the C library). */
+double oracle_log_crisp(double x) {
+  const double sqrt2 = 0x1.6a09e667f3bcdp+0;
+  const double ln2_hi = 0x1.62e42ff000000p-1;
+  const double ln2_lo = -0x1.718432a1b0e26p-35;
+  uint64_t bits;
+  memcpy(&bits, &x, sizeof bits);
+  int e = (int)((bits >> 52) & 0x7ff) - 1023;
+  bits = (bits & 0x000fffffffffffffULL) | 0x3ff0000000000000ULL;
+  double m;
+  memcpy(&m, &bits, sizeof m); /* m in [1, 2) */
+  if (m > sqrt2) {
+    m = m * 0.5;
+    e += 1;
+  }
+  const double s = (m - 1.0) / (m + 1.0);
+  const double s2 = s * s;
+  double p = 1.0 / 23.0;
+  p = fma(p, s2, 1.0 / 21.0);
+  p = fma(p, s2, 1.0 / 19.0);
+  p = fma(p, s2, 1.0 / 17.0);
+  p = fma(p, s2, 1.0 / 15.0);
+  p = fma(p, s2, 1.0 / 13.0);
+  p = fma(p, s2, 1.0 / 11.0);
+  p = fma(p, s2, 1.0 / 9.0);
+  p = fma(p, s2, 1.0 / 7.0);
+  p = fma(p, s2, 1.0 / 5.0);
+  p = fma(p, s2, 1.0 / 3.0);
+  p = fma(p, s2, 1.0);
+  const double lm = (2.0 * s) * p;
+  const double r = fma((double)e, ln2_lo, lm);
+  return fma((double)e, ln2_hi, r);
+}
+
+void oracle_log_crisp_array(const double* x, double* y, int64_t count) {
+  for (int64_t i = 0; i < count; ++i) y[i] = oracle_log_crisp(x[i]);
+}
+
+/* J = sum_b rne(t_b 2^52) of two fixed-point distributions p (total Tp) and
+ * a (total Ta) over nb blocks.  Returns J; JSD = J 2^-53. */
+int64_t oracle_jsd_fixed(int64_t nb, const int64_t* p, int64_t Tp, const int64_t* a, int64_t Ta) {
+  int64_t J = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    const double P = (double)p[b] / (double)Tp;
+    const double Q = (double)a[b] / (double)Ta;
+    const double M = 0.5 * (P + Q);
+    const double tp = P > 0.0 ? P * oracle_log_crisp(P / M) : 0.0;
+    const double tq = Q > 0.0 ? Q * oracle_log_crisp(Q / M) : 0.0;
+    const double t = tp + tq;
+    J += (int64_t)llrint(ldexp(t, 52));
+  }
+  return J;
+}
+
+/* The pooled estimate of one query head's last query block: Qbar over the
+ * last block's rows, Kbar over every key block (sequential fp32 sums, then
+ * divided by the row count), z_b = fl(fma-chain(Qbar, Kbar_b) c), row max,
+ * exp_crisp, int64 row sum, abar_b = rne(fl(e_b / l) 2^40).  Writes abar [nb]
+ * and returns its total. */
+int64_t oracle_pooled_last_row(int64_t n, int32_t d, int32_t B, const float* Qh, const float* Kh,
+                               int64_t* abar) {
+  const int64_t nb = (n + B - 1) / B;
+  const float c = oracle_scale(d);
+  float* qbar = (float*)malloc(sizeof(float) * d);
+  float* kbar = (float*)malloc(sizeof(float) * d);
+  float* z = (float*)malloc(sizeof(float) * nb);
+  const int64_t q0 = (nb - 1) * B, qcnt = n - q0;
+  for (int32_t k = 0; k < d; ++k) {
+    float s = 0.0f;
+    for (int64_t r = 0; r < qcnt; ++r) s = s + Qh[(size_t)(q0 + r) * d + k];
+    qbar[k] = s / (float)qcnt;
+  }
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t r0 = b * B;
+    const int64_t cnt = (r0 + B <= n) ? B : n - r0;
+    for (int32_t k = 0; k < d; ++k) {
+      float s = 0.0f;
+      for (int64_t r = 0; r < cnt; ++r) s = s + Kh[(size_t)(r0 + r) * d + k];
+      kbar[k] = s / (float)cnt;
+    }
+    float acc = 0.0f;
+    for (int32_t k = 0; k < d; ++k) acc = fmaf(qbar[k], kbar[k], acc);
+    z[b] = acc * c;
+  }
+  float m = z[0];
+  for (int64_t b = 1; b < nb; ++b)
+    if (z[b] > m) m = z[b];
+  int64_t L = 0;
+  for (int64_t b = 0; b < nb; ++b) L += fix_rne(oracle_exp_crisp(z[b] - m));
+  const float l = fix_to_float(L);
+  int64_t T = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    abar[b] = fix_rne(oracle_exp_crisp(z[b] - m) / l);
+    T += abar[b];
+  }
+  free(qbar);
+  free(kbar);
+  free(z);
+  return T;
 }
 
 /* ---------------------------------------------------- masked attention -- */

@@ -143,6 +143,40 @@ def test_alpha_variants(alpha):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", [crisp.SELECT_NOISE_FLOOR, crisp.SELECT_CUMULATIVE])
+def test_gamma_variant(mode):
+    """gamma = 97/100, the pages' wider coverage: PE index sets (and, in the cumulative mode,
+    the VS lists) bit-exact against the oracle; a larger gamma never keeps fewer blocks."""
+    import dataclasses
+    wl, I, X, spec, bufs, ref = _case("llama_32k", select_mode=mode)
+    spec_g = dataclasses.replace(spec, gamma=(97, 100))
+    b2 = run_route_select(spec_g, X)
+    gpu = download_index_sets(b2)
+    base = download_index_sets(bufs)
+    pr = ref["proxy"]
+    G = wl.hq // wl.hkv
+    assert np.array_equal(gpu["route"], pr["route"])
+    checked = 0
+    for h in range(wl.hq):
+        g, b = gpu["heads"][h], base["heads"][h]
+        if pr["route"][h]:
+            if mode != crisp.SELECT_CUMULATIVE:
+                continue
+            for key, mk in (("vertical", "mass_v"), ("slash", "mass_s")):
+                want = oracle.cumulative_select(pr[mk][h], pr["total"][h], (97, 100))
+                assert np.array_equal(g[key], want), (h, key)
+                assert set(b[key].tolist()) <= set(want.tolist()), (h, key)
+        else:
+            if checked >= 4:  # the oracle's PE index is the slow part; four heads span both KV groups
+                continue
+            rowptr, cols = oracle.pe_index(I.q[h], I.k[h // G], wl.block, (97, 100))
+            assert np.array_equal(g["rowptr"], rowptr), h
+            assert np.array_equal(g["cols"], cols), h
+            assert g["rowptr"][-1] >= b["rowptr"][-1], h
+            checked += 1
+
+
+@pytest.mark.timeout(600)
 def test_determinism():
     wl, I, X, spec, bufs, ref = _case("llama_32k")
     import torch

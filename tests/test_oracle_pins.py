@@ -462,3 +462,122 @@ def test_generator_bf16_storage():
         assert np.all((a.view(np.uint32) & 0xFFFF) == 0)
     bits = synth.to_bf16_bits(I.q)
     assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), I.q)
+
+
+# -------------------------------------------------------- divergence router ----
+def test_log_crisp_within_3ulp_of_log(oracle_lib):
+    """Measured bound of the reduction + atanh series: 3 ulp where ln x is small against x
+    (m just above 1), 2 ulp elsewhere."""
+    rng = np.random.default_rng(31)
+    x = np.concatenate([
+        np.exp(rng.uniform(-690.0, 690.0, 200000)),  # wide exponent range
+        rng.uniform(0.5, 2.0, 200000),  # around the reduction boundaries
+        1.0 + rng.uniform(-1e-6, 1e-6, 20000),  # near the zero of ln
+        np.sqrt(2.0) * (1.0 + np.arange(-50, 51) * 2.0 ** -52),  # the sqrt(2) switch
+        2.0 ** np.arange(-1020, 1020, dtype=np.float64), [1.0, 2.0, 0.5, math.e],
+    ])
+    y = oracle.log_crisp(x)
+    ref = np.log(x)
+    assert oracle.log_crisp(np.array([1.0]))[0] == 0.0  # exact zero keeps identical distributions at JSD 0
+    ulp = np.spacing(np.abs(ref))
+    err = np.abs(y - ref)
+    # near x = 1 the result is tiny: measure those against the ulp of x - 1 instead
+    bound = np.where(np.abs(ref) < 1e-3, np.spacing(np.abs(x - 1.0) + 1e-300) * 4, 3 * ulp)
+    assert np.all(err <= bound), (x[err > bound][:5], err[err > bound][:5])
+
+
+def _rand_fixed(rng, nb, zero_frac=0.0, total=128 * FIX):
+    w = rng.gamma(0.3, 1.0, nb)
+    w[rng.random(nb) < zero_frac] = 0.0
+    if w.sum() == 0:
+        w[0] = 1.0
+    return np.floor(w / w.sum() * total).astype(np.int64)
+
+
+def test_jsd_matches_scipy_jensenshannon(oracle_lib):
+    from scipy.spatial.distance import jensenshannon
+    rng = np.random.default_rng(32)
+    for trial in range(60):
+        nb = int(rng.integers(2, 3000))
+        p = _rand_fixed(rng, nb, zero_frac=0.2 if trial % 3 == 0 else 0.0)
+        a = _rand_fixed(rng, nb, zero_frac=0.3 if trial % 4 == 1 else 0.0, total=FIX)
+        J = oracle.jsd_fixed(p, p.sum(), a, a.sum())
+        ref = jensenshannon(p / p.sum(), a / a.sum()) ** 2  # scipy returns the distance (square root)
+        assert abs(J * 2.0 ** -53 - ref) < 1e-12, (trial, J * 2.0 ** -53, ref)
+
+
+def test_jsd_closed_forms(oracle_lib):
+    # identical distributions: zero exactly
+    rng = np.random.default_rng(33)
+    p = _rand_fixed(rng, 500)
+    assert oracle.jsd_fixed(p, p.sum(), p, p.sum()) == 0
+    # the same distribution at another scale is still identical
+    assert oracle.jsd_fixed(p, p.sum(), 4 * p, 4 * p.sum()) == 0
+    # disjoint supports: ln 2
+    a = np.zeros_like(p)
+    a[p == 0] = 1
+    p2 = p.copy()
+    p2[:] = 0
+    p2[:250] = 3
+    a2 = np.zeros_like(p)
+    a2[250:] = 7
+    J = oracle.jsd_fixed(p2, p2.sum(), a2, a2.sum())
+    # each of the N_b terms is rounded to 2^-52 once: JSD moves by at most N_b 2^-54
+    assert abs(J * 2.0 ** -53 - math.log(2.0)) <= len(p2) * 2.0 ** -54 + 1e-15
+    # two points: P = (x, 1-x), Q = (y, 1-y), written out
+    for x, y in ((0.25, 0.75), (0.5, 0.125), (0.9, 0.1), (1e-6, 0.5)):
+        P = np.array([x, 1 - x])
+        Q = np.array([y, 1 - y])
+        M = (P + Q) / 2
+        ref = 0.5 * np.sum(P * np.log(P / M)) + 0.5 * np.sum(Q * np.log(Q / M))
+        pf = np.array([round(x * FIX), FIX - round(x * FIX)], np.int64)
+        qf = np.array([round(y * FIX), FIX - round(y * FIX)], np.int64)
+        J = oracle.jsd_fixed(pf, FIX, qf, FIX)
+        assert abs(J * 2.0 ** -53 - ref) < 1e-11, (x, y)
+    # symmetric, bit for bit
+    q = _rand_fixed(rng, 500, total=FIX)
+    assert oracle.jsd_fixed(p, p.sum(), q, q.sum()) == oracle.jsd_fixed(q, q.sum(), p, p.sum())
+
+
+@pytest.mark.parametrize("n,B", [(1000, 64), (4096, 64), (300, 128)])
+def test_pooled_row_is_last_row_of_pe_map(oracle_lib, n, B):
+    """The divergence router's pooled estimate is Alg. 4's pooled map at the last query block."""
+    rng = np.random.default_rng(34)
+    d = 32
+    q = (rng.standard_normal((n, d)) * 2).astype(np.float32)
+    k = (rng.standard_normal((n, d)) * 2).astype(np.float32)
+    abar, ta = oracle.pooled_last_row(q, k, B)
+    _, _, full, _, _ = oracle.pe_index(q, k, B, (19, 20), want_abar=True)
+    nb = (n + B - 1) // B
+    assert np.array_equal(abar, full[nb * (nb - 1) // 2:])
+    assert ta == abar.sum()
+    # Q = 0: every pooled score is 0, so the estimate is uniform: rne(fl(1/N_b) 2^40)
+    z, _ = oracle.pooled_last_row(np.zeros_like(q), k, B)
+    assert np.all(z == np.int64(np.rint(np.float32(1.0) / np.float32(nb) * np.float64(FIX))))
+
+
+def test_jsd_route_matches_fp64_writing_and_separates_heads(oracle_lib):
+    """The router end to end on the small planted layer against a plain fp64 writing of
+    the same definitions; the planted head diverges, the i.i.d. head does not."""
+    wl = synth.WORKLOADS["tiny"]
+    I = synth.make_inputs(wl)
+    B, nb = wl.block, (wl.n + wl.block - 1) // wl.block
+    pr = oracle.proxy(I.q, I.k, B, wl.w_sink, wl.w_local, synth.TAU, I.bias_offsets, I.bias_values)
+    out = oracle.jsd_route(I.q, I.k, B, pr)
+    G = wl.hq // wl.hkv
+    for h in range(wl.hq):
+        q = I.q[h].astype(np.float64)
+        k = I.k[h // G].astype(np.float64)
+        qbar = q[(nb - 1) * B:].mean(0)
+        kbar = np.stack([k[b * B:(b + 1) * B].mean(0) for b in range(nb)])
+        z = kbar @ qbar / math.sqrt(wl.d)
+        Q = np.exp(z - z.max())
+        Q /= Q.sum()
+        P = pr["mass_v"][h] / pr["total"][h]
+        M = (P + Q) / 2
+        ref = 0.5 * np.sum(P[P > 0] * np.log(P[P > 0] / M[P > 0])) + 0.5 * np.sum(Q * np.log(Q / M))
+        got = out["jsd"][h] * 2.0 ** -53
+        assert abs(got - ref) < 1e-6 * max(ref, 1e-3), (h, got, ref)
+        assert np.abs(out["abar"][h] / out["abar_total"][h] - Q).max() < 1e-6
+    assert out["route"].tolist() == [1 if h in wl.planted_heads else 0 for h in range(wl.hq)]
+    assert out["route"].tolist() == pr["route"].tolist()
