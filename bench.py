@@ -312,6 +312,15 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
         res["dense_ms"] = sum(time_calls(lambda: crisp.dense_prefill(spec, q, k, v, od, bufs, bo, bv), dense_reps,
                                          stream)) / dense_reps
     res["tiles"] = tile_counts(bufs, spec)
+    # the divergence router on the same proxy: its extra cost and its agreement with C_struct
+    rj = torch.zeros(spec.heads, dtype=torch.uint8, device="cuda")
+    jj = torch.zeros(spec.heads, dtype=torch.int64, device="cuda")
+    route()
+    crisp.route_jsd(spec, q, k, bufs, rj, jj)
+    t_jsd = time_calls(lambda: crisp.route_jsd(spec, q, k, bufs, rj, jj), 5, stream)
+    res["jsd_router"] = {"extra_ms": round(sum(t_jsd) / len(t_jsd), 4),
+                         "agreement_with_cstruct": float((rj == bufs.route).float().mean().item()),
+                         "tau_jsd": "1/100"}
     del q, k, v, o
     torch.cuda.empty_cache()
     return res
@@ -383,6 +392,9 @@ def main():
                      "flops_per_launch": flops},
         "context": {"pages_attention_speedup_512k": "up to 5.30x (real model maps; hardware not stated)"},
     }
+    out["jsd_router"] = dict(r["jsd_router"], cstruct_router_ms=round(st["route"], 3),
+                             note="route = proxy map + block masses + C_struct; the divergence router needs "
+                                  "the same proxy plus extra_ms (block means, pooled row, softmax, JSD)")
     if "dense_ms" in r:
         out["dense_ms_per_layer"] = round(r["dense_ms"], 3)
         out["speedup_vs_dense"] = round(r["dense_ms"] / total_ms, 3)

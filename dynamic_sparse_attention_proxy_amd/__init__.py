@@ -22,7 +22,7 @@ STATUS = {0: "CRISP_OK", -1: "CRISP_ERR_NULL", -2: "CRISP_ERR_SHAPE", -3: "CRISP
           -8: "CRISP_ERR_ALIGN"}
 
 EXPORTS = ["crisp_workspace_size", "crisp_index_capacity", "crisp_route", "crisp_select_indices",
-           "crisp_sparse_prefill", "crisp_dense_prefill", "crisp_status_string"]
+           "crisp_sparse_prefill", "crisp_dense_prefill", "crisp_route_jsd", "crisp_status_string"]
 
 
 class Shape(ctypes.Structure):
@@ -80,6 +80,9 @@ def load_library(path: str = None):
         lib.crisp_sparse_prefill.restype = ctypes.c_int
         lib.crisp_dense_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), P, ctypes.c_size_t, P, P]
         lib.crisp_dense_prefill.restype = ctypes.c_int
+        lib.crisp_route_jsd.argtypes = [S, C, ctypes.c_uint32, ctypes.c_uint32, P, P, ctypes.POINTER(IndexSets), P,
+                                        ctypes.c_size_t, P, P, P, P]
+        lib.crisp_route_jsd.restype = ctypes.c_int
         lib.crisp_status_string.argtypes = [ctypes.c_int]
         lib.crisp_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -214,6 +217,19 @@ def dense_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None,
                                               q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(b),
                                               bufs.ws.data_ptr(), bufs.ws_bytes, o.data_ptr(), _stream(stream)),
            "crisp_dense_prefill")
+
+
+def route_jsd(spec: LayerSpec, q, k, bufs: Buffers, route_out, jsd_out, tau_jsd=(1, 100), pooled_out=None,
+              stream=None):
+    """crisp_route_jsd: the divergence router on the proxy that ``route`` left in ``bufs``.
+    route_out [BH] uint8, jsd_out [BH] int64 (JSD = value * 2^-53), pooled_out [BH, N_b]
+    int64 or None."""
+    idx = bufs.index_sets()
+    _check(load_library().crisp_route_jsd(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), tau_jsd[0],
+                                          tau_jsd[1], q.data_ptr(), k.data_ptr(), ctypes.byref(idx),
+                                          bufs.ws.data_ptr(), bufs.ws_bytes, route_out.data_ptr(), jsd_out.data_ptr(),
+                                          None if pooled_out is None else pooled_out.data_ptr(), _stream(stream)),
+           "crisp_route_jsd")
 
 
 def prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):

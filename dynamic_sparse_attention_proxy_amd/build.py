@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "crisp")
 LIB = os.path.join(HERE, "libcrisp.so")
-SOURCES = ["route.hip", "select.hip", "attention.hip", "abi.hip"]
+SOURCES = ["route.hip", "select.hip", "jsd.hip", "attention.hip", "abi.hip"]
 # per-source extra flags: the attention kernels never produce or test NaN, so max
 # needs no NaN canonicalisation
 EXTRA = {"attention.hip": ["-fno-honor-nans"]}

@@ -26,6 +26,8 @@ struct Layout {
   size_t s_qbar, s_kbar, s_zbar, s_abar, s_rowtot, s_hist, s_state, s_gt, s_tie, s_tiep, s_end;
   // attention
   size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_vt, a_qcnt, a_end;
+  // divergence router
+  size_t j_qbar, j_kbar, j_zbar, j_abar, j_end;
   size_t total;
 };
 
@@ -116,9 +118,21 @@ Layout layout(const Dims& d) {
   o = align_up(o + 8 * sizeof(int));  // work-queue counters
   L.a_end = o;
 
+  o = 0;
+  L.j_qbar = o;
+  o = align_up(o + (size_t)d.bh * d.d * sizeof(float));
+  L.j_kbar = o;
+  o = align_up(o + (size_t)d.bkv * d.nb * d.d * sizeof(float));
+  L.j_zbar = o;
+  o = align_up(o + (size_t)d.bh * d.nb * sizeof(float));
+  L.j_abar = o;
+  o = align_up(o + (size_t)d.bh * d.nb * sizeof(long long));
+  L.j_end = o;
+
   L.total = L.r_end;
   if (L.s_end > L.total) L.total = L.s_end;
   if (L.a_end > L.total) L.total = L.a_end;
+  if (L.j_end > L.total) L.total = L.j_end;
   return L;
 }
 
@@ -319,6 +333,37 @@ crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* c
   (void)hipGetLastError();
   if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, nullptr, nullptr, w + L.a_vt,
                        reinterpret_cast<int*>(w + L.a_qcnt), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return CRISP_ERR_HIP;
+  return hip_status();
+}
+
+crisp_status crisp_route_jsd(const crisp_shape* shape, const crisp_config* cfg, uint32_t tau_num,
+                             uint32_t tau_den, const void* q, const void* k, const crisp_index_sets* idx,
+                             void* ws, size_t ws_bytes, uint8_t* route_jsd, int64_t* jsd, int64_t* pooled,
+                             void* stream) {
+  Dims d;
+  CRISP_TRY(make_dims(shape, cfg, &d));
+  if (tau_den == 0) return CRISP_ERR_CONFIG;
+  CRISP_TRY(check_tensor(q));
+  CRISP_TRY(check_tensor(k));
+  CRISP_TRY(check_tensor(ws));
+  if (!idx || !idx->mass_v || !idx->mass_total || !route_jsd || !jsd) return CRISP_ERR_NULL;
+  if (!aligned(idx->mass_v, 8) || !aligned(idx->mass_total, 8) || !aligned(jsd, 8) ||
+      (pooled && !aligned(pooled, 8)))
+    return CRISP_ERR_ALIGN;
+  const Layout L = layout(d);
+  if (ws_bytes < L.total) return CRISP_ERR_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  JsdScratch js;
+  js.qbar = reinterpret_cast<float*>(w + L.j_qbar);
+  js.kbar = reinterpret_cast<float*>(w + L.j_kbar);
+  js.zbar = reinterpret_cast<float*>(w + L.j_zbar);
+  js.abar = reinterpret_cast<long long*>(w + L.j_abar);
+  (void)hipGetLastError();
+  if (launch_route_jsd(d, tau_num, tau_den, q, k, js, reinterpret_cast<const long long*>(idx->mass_v),
+                       reinterpret_cast<const long long*>(idx->mass_total), route_jsd,
+                       reinterpret_cast<long long*>(jsd), reinterpret_cast<long long*>(pooled),
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }

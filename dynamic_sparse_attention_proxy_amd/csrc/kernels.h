@@ -54,6 +54,13 @@ struct SelectScratch {
   int* tiepre;         // [bh][nb]
 };
 
+struct JsdScratch {
+  float* qbar;      // [bh][d] block mean of the last query block
+  float* kbar;      // [bkv][nb][d] block means of every key block
+  float* zbar;      // [bh][nb] pooled scores of the last query block
+  long long* abar;  // [bh][nb] quantised pooled estimate
+};
+
 struct IndexOut {
   uint8_t* route;
   long long* cstruct_num;
@@ -74,6 +81,10 @@ hipError_t launch_route(const Dims& dm, const RouteArgs& ra, const BiasArgs& bia
 // select.hip
 hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, const void* k,
                          const SelectScratch& ws, const IndexOut& io, hipStream_t st);
+// jsd.hip: the divergence router; reads mass_v / mass_total written by launch_route
+hipError_t launch_route_jsd(const Dims& dm, unsigned tau_num, unsigned tau_den, const void* q, const void* k,
+                            const JsdScratch& ws, const long long* mass_v, const long long* mass_total,
+                            uint8_t* route_jsd, long long* jsd, long long* pooled, hipStream_t st);
 // attention.hip
 bool use_matrix_engine(const Dims& dm);  // bf16, d = 128, B = 128
 // tile lists: for the matrix engine the lists of query-head pairs [bkv * pairs][ntri]

@@ -13,6 +13,8 @@
  *   crisp_select_indices  VS vertical/slash block lists or the PE block set
  *   crisp_sparse_prefill  attention over the selected blocks
  *   crisp_dense_prefill   full causal attention with the same tile engine
+ * and, for comparison, crisp_route_jsd: the Jensen-Shannon divergence router
+ * that C_struct replaces, evaluated on the same proxy after crisp_route.
  *
  * Conventions shared by every call
  *   - Tensors are caller-owned device memory, contiguous, row-major:
@@ -126,8 +128,8 @@ typedef struct {
 } crisp_index_sets;
 
 /* Scratch bytes needed by crisp_route, crisp_select_indices,
- * crisp_sparse_prefill and crisp_dense_prefill for this shape (0 if the
- * arguments are invalid). */
+ * crisp_sparse_prefill, crisp_dense_prefill and crisp_route_jsd for this
+ * shape (0 if the arguments are invalid). */
 size_t crisp_workspace_size(const crisp_shape* shape, const crisp_config* cfg);
 
 /* Per-head capacity pe_col needs: N_b (N_b + 1) / 2 (-1 if invalid). */
@@ -168,6 +170,30 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
 crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
                                  const void* k, const void* v, const crisp_rel_bias* bias, void* ws,
                                  size_t ws_bytes, void* o, void* stream);
+
+/* The divergence router the pages contrast with C_struct (summary page,
+ * Motivation: a second, pooled estimate of the head's attention, its
+ * Jensen-Shannon divergence from the per-query one, VS above a threshold).
+ * Run after crisp_route on the same idx: it reads idx->mass_v and
+ * idx->mass_total (the per-query estimate P_b = mass_v[b] / mass_total, the
+ * proxy map pooled after the softmax) and q, k.  The pooled estimate Q is the
+ * softmax over key blocks of fl(Qbar . Kbar_b) * c, with Qbar the mean of the
+ * last query block's rows and Kbar_b the mean of key block b (fp32 sums in
+ * row order; the last row of the PE path's pooled map), in the same 2^40
+ * fixed point.  JSD = (KL(P||M) + KL(Q||M)) / 2, M = (P + Q) / 2, natural log,
+ * with per-block terms t_b computed in fp64 and summed as rne(t_b 2^52).
+ * Writes, per head (BH entries):
+ *   jsd[h]       int64 J with JSD = J * 2^-53 (nats)
+ *   route_jsd[h] 1 (VS) iff tau_den * J >= tau_num * 2^53, i.e. JSD >= tau
+ *   pooled[h][b] optional ([BH][N_b] int64, may be NULL): the quantised pooled
+ *                estimate rne(Q_b 2^40)
+ * Uses ws as scratch (it may overwrite what crisp_route left there; the
+ * routing outputs live in idx).  tau_den = 0 gives CRISP_ERR_CONFIG; jsd and
+ * pooled must be 8-byte aligned. */
+crisp_status crisp_route_jsd(const crisp_shape* shape, const crisp_config* cfg, uint32_t tau_num,
+                             uint32_t tau_den, const void* q, const void* k, const crisp_index_sets* idx,
+                             void* ws, size_t ws_bytes, uint8_t* route_jsd, int64_t* jsd, int64_t* pooled,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* crisp_status_string(crisp_status status);

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("crisp_route", "crisp_select_indices", "crisp_sparse_prefill", "crisp_dense_prefill"):
+    for n in ("crisp_route", "crisp_select_indices", "crisp_sparse_prefill", "crisp_dense_prefill",
+              "crisp_route_jsd"):
         assert n in names
     assert sorted(crisp.EXPORTS) == names
 
@@ -96,6 +97,28 @@ def test_null_alignment_workspace_capacity(lib):
                                     None) == -1
     assert lib.crisp_dense_prefill(sh, cf, fake, fake, fake, None, fake, ws - 1, fake, None) == -5
     assert lib.crisp_dense_prefill(sh, cf, fake, fake, fake, None, None, ws, fake, None) == -1
+
+
+def test_route_jsd_validation(lib):
+    """The divergence router's argument checks (no launch is reached)."""
+    s = _spec()
+    sh, cf = ctypes.byref(s.shape()), ctypes.byref(s.config())
+    fake = ctypes.c_void_p(1 << 20)
+    ws = crisp.workspace_size(s)
+    idx = crisp.IndexSets(*([1 << 20] * 10), crisp.index_capacity(s))
+    f = lib.crisp_route_jsd
+    assert f(sh, cf, 1, 0, fake, fake, ctypes.byref(idx), fake, ws, fake, fake, None, None) == -4
+    assert f(sh, cf, 1, 100, fake, fake, None, fake, ws, fake, fake, None, None) == -1
+    assert f(sh, cf, 1, 100, fake, fake, ctypes.byref(idx), fake, ws, None, fake, None, None) == -1
+    assert f(sh, cf, 1, 100, fake, fake, ctypes.byref(idx), fake, ws, fake, None, None, None) == -1
+    assert f(sh, cf, 1, 100, fake, fake, ctypes.byref(idx), fake, ws, fake, ctypes.c_void_p((1 << 20) + 4), None,
+             None) == -8
+    assert f(sh, cf, 1, 100, fake, fake, ctypes.byref(idx), fake, ws - 1, fake, fake, None, None) == -5
+    nomass = crisp.IndexSets(*([1 << 20] * 2), None, *([1 << 20] * 7), crisp.index_capacity(s))
+    assert f(sh, cf, 1, 100, fake, fake, ctypes.byref(nomass), fake, ws, fake, fake, None, None) == -1
+    bad = _spec(head_dim=96)
+    assert f(ctypes.byref(bad.shape()), ctypes.byref(bad.config()), 1, 100, fake, fake, ctypes.byref(idx), fake, ws,
+             fake, fake, None, None) == -2
 
 
 def test_select_modes(lib):

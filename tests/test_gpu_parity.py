@@ -73,6 +73,26 @@ def _check_attention(wl, I, X, spec, bufs, ref, rows, what, heads=None):
 
 ALL = ["tiny", "llama_32k", "llama_128k", "qwen_128k", "llama_512k"]
 
+JSD_TAU = (1, 100)
+
+
+def _check_jsd(wl, I, X, spec, bufs, ref):
+    """crisp_route_jsd on the proxy that crisp_route left in bufs, against the oracle's
+    divergence router on the oracle's own block masses: bit-exact J, route and pooled row."""
+    import torch
+    bh, nb = spec.heads, spec.num_blocks
+    r_gpu = torch.zeros(bh, dtype=torch.uint8, device="cuda")
+    j_gpu = torch.zeros(bh, dtype=torch.int64, device="cuda")
+    p_gpu = torch.zeros(bh, nb, dtype=torch.int64, device="cuda")
+    crisp.route_jsd(spec, X.q, X.k, bufs, r_gpu, j_gpu, JSD_TAU, p_gpu)
+    torch.cuda.synchronize()
+    with Timer("oracle jsd"):
+        want = oracle.jsd_route(I.q, I.k, wl.block, ref["proxy"], JSD_TAU)
+    assert np.array_equal(p_gpu.cpu().numpy(), want["abar"]), "pooled estimate"
+    assert np.array_equal(j_gpu.cpu().numpy(), want["jsd"]), (j_gpu.cpu().numpy()[:4], want["jsd"][:4])
+    assert np.array_equal(r_gpu.cpu().numpy(), want["route"])
+    return want
+
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ALL)
@@ -92,6 +112,17 @@ def test_index_sets_bit_exact(name):
         # every row of two VS and two PE heads (both kinds of KV group)
         _check_attention(wl, I, X, spec, bufs, ref, None, f"{name} all rows, heads 0 1 16 17",
                          heads=[0, 1, 16, 17])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ALL[::-1])  # the largest case is still cached from the test above
+def test_jsd_router(name):
+    """The divergence router bit-exact against the oracle; on the planted layers it makes
+    the same decisions as C_struct (planted heads diverge from their pooled estimate)."""
+    wl, I, X, spec, bufs, ref = _case(name)
+    want = _check_jsd(wl, I, X, spec, bufs, ref)
+    log(name, "JSD (nats) per head", (want["jsd"] * 2.0 ** -53).round(5).tolist())
+    assert want["route"].tolist() == ref["proxy"]["route"].tolist()
 
 
 @pytest.mark.timeout(600)
@@ -222,6 +253,8 @@ def test_edge_shapes(name, mode):
     gpu = download_index_sets(bufs)
     bad = compare_index_sets(gpu, ref)
     assert not bad, "\n".join(bad[:20])
+    if mode == crisp.SELECT_NOISE_FLOOR:
+        _check_jsd(wl, I, X, spec, bufs, ref)
     _check_attention(wl, I, X, spec, bufs, ref, None, f"{name} mode {mode}")
     if mode == crisp.SELECT_KEEP_ALL:
         import torch
