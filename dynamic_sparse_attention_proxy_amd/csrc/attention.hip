@@ -417,14 +417,22 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
               }
             }
             if (masked) {
+              // the kept keys of a row form one range: C <= rr (lower part) and / or
+              // C > rr (upper part), and C < nl (inside the sequence); an empty range
+              // is moved past every C
               const bool lower_ok = (mode & kModeLower) != 0;
               const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
-              const int nl = dm.n - kb * B - 8 * hl;  // key inside the sequence  <=>  C < nl
+              const int nl = dm.n - kb * B - 8 * hl;
+              int lo = lower_ok ? 0 : rr + 1;
+              int hi = upper_ok ? nl - 1 : min(rr, nl - 1);
+              if (hi < lo) lo = 1 << 20, hi = lo;
+              const unsigned span = (unsigned)(hi - lo);
+              int nlo = -lo;
+              asm volatile("" : "+v"(nlo));
 #pragma unroll
               for (int x = 0; x < 16; ++x) {
                 const int C = 32 * a + 16 * (x >> 3) + (x & 7);
-                const bool keep = (rr >= C ? lower_ok : upper_ok) && C < nl;
-                if (!keep) s[x] = -__builtin_inff();
+                if ((unsigned)(C + nlo) > span) s[x] = -__builtin_inff();
               }
             }
           }
