@@ -28,6 +28,52 @@ __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p) {
   return bf16_to_f32(*p);
 }
 
+// Eight consecutive columns of one row as fp32 (16-byte aligned source).
+__device__ __forceinline__ void load8(const bf16_t* p, float* x) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+  x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+}
+
+// Column means of cnt consecutive rows (row stride d): eight columns starting at
+// p, each an fp32 sum over the rows in ascending order, then one division by
+// the row count.
+template <typename T>
+__device__ __forceinline__ void mean8(const T* p, int d, int cnt, float* out) {
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.0f;
+  int r = 0;
+  for (; r + 4 <= cnt; r += 4) {
+    float x[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load8(p + (size_t)(r + j) * d, x[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = s[i] + x[j][i];
+  }
+  for (; r < cnt; ++r) {
+    float x[8];
+    load8(p + (size_t)r * d, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = s[i] + x[i];
+  }
+  const float fc = (float)cnt;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = s[i] / fc;
+}
+
 // e^x for x <= 0 in fp32, bit-identical by construction to the reference
 // definition: Cody-Waite reduction x = k ln2 + r (k = rint(x log2 e), ln2 in a
 // 15-bit head and a tail), Taylor polynomial of degree 7 in Horner form with

@@ -23,23 +23,6 @@ namespace {
 
 constexpr int kJsdShift = 52;  // divergence terms: rne(t 2^52); JSD = J 2^-53
 
-// Eight consecutive columns of one row as fp32.
-__device__ __forceinline__ void load8(const bf16_t* p, float* x) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const unsigned w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void load8(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
-  x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
-}
-
 // Block means, sequential fp32 sums over rows in ascending order, then one
 // division by the row count.  Unit u < bh: the last query block of query head
 // u; otherwise key block (u - bh) % nb of KV head (u - bh) / nb.  A thread owns
@@ -70,30 +53,8 @@ __global__ __launch_bounds__(256) void jsd_pool_kernel(Dims dm, const T* __restr
     r0 = b * dm.B;
     cnt = min(dm.B, dm.n - r0);
   }
-  const T* p = src + (size_t)r0 * dm.d + c0;
-  float s[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = 0.0f;
-  int r = 0;
-  for (; r + 4 <= cnt; r += 4) {
-    float x[4][8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) load8(p + (size_t)(r + j) * dm.d, x[j]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = s[i] + x[j][i];
-  }
-  for (; r < cnt; ++r) {
-    float x[8];
-    load8(p + (size_t)r * dm.d, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] = s[i] + x[i];
-  }
-  const float fc = (float)cnt;
   float out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = s[i] / fc;
+  mean8(src + (size_t)r0 * dm.d + c0, dm.d, cnt, out);
   float4* o4 = reinterpret_cast<float4*>(dst + c0);
   o4[0] = make_float4(out[0], out[1], out[2], out[3]);
   o4[1] = make_float4(out[4], out[5], out[6], out[7]);

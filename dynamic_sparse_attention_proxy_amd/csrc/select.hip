@@ -175,10 +175,18 @@ __device__ __forceinline__ bool group_has_pe(const IndexOut& io, const Dims& dm,
 }
 
 // Block means: Qbar[qb][k] = fl(sum over rows ascending) / cnt; same for K.
+// Unit u = y * nb + qb: query head y < bh (PE heads only) or KV head y - bh
+// (groups with a PE head); a thread owns eight columns of one unit, so the
+// d / 8 threads of a unit read each row as contiguous 16-byte pieces.
 template <typename T>
-__global__ void pe_pool_kernel(Dims dm, const T* __restrict__ q, const T* __restrict__ k, IndexOut io,
-                               float* __restrict__ qbar, float* __restrict__ kbar) {
-  const int qb = blockIdx.x, y = blockIdx.y, kk = threadIdx.x;
+__global__ __launch_bounds__(256) void pe_pool_kernel(Dims dm, const T* __restrict__ q, const T* __restrict__ k,
+                                                      IndexOut io, float* __restrict__ qbar,
+                                                      float* __restrict__ kbar) {
+  const int tpu = dm.d / 8;
+  const long long units = (long long)(dm.bh + dm.bkv) * dm.nb;
+  const long long u = (long long)blockIdx.x * (256 / tpu) + threadIdx.x / tpu;
+  if (u >= units) return;
+  const int y = (int)(u / dm.nb), qb = (int)(u % dm.nb);
   const T* src;
   float* dst;
   if (y < dm.bh) {
@@ -192,10 +200,12 @@ __global__ void pe_pool_kernel(Dims dm, const T* __restrict__ q, const T* __rest
     dst = kbar + ((size_t)kvh * dm.nb + qb) * dm.d;
   }
   const int r0 = qb * dm.B;
-  const int cnt = min(dm.B, dm.n - r0);
-  float s = 0.0f;
-  for (int r = 0; r < cnt; ++r) s = s + load_f32(src + (size_t)(r0 + r) * dm.d + kk);
-  dst[kk] = s / (float)cnt;
+  const int c0 = (threadIdx.x % tpu) * 8;
+  float out[8];
+  mean8(src + (size_t)r0 * dm.d + c0, dm.d, min(dm.B, dm.n - r0), out);
+  float4* o4 = reinterpret_cast<float4*>(dst + c0);
+  o4[0] = make_float4(out[0], out[1], out[2], out[3]);
+  o4[1] = make_float4(out[4], out[5], out[6], out[7]);
 }
 
 // Pooled scores, 64 x 64 tile per block, 4 x 4 per thread, chunk of 32 over d.
@@ -353,14 +363,41 @@ __global__ __launch_bounds__(kThreads) void pe_radix_hist_kernel(Dims dm, IndexO
   const int hi = shift + width;
   for (int i = tid; i < kHistBins; i += kThreads) cnt[i] = 0, mass[i] = 0;
   __syncthreads();
+  // a thread scans runs of 16 consecutive values and adds each run of equal
+  // digits to LDS once: neighbouring entries of a row of the pooled map are
+  // close in value, so most runs collapse (pass 0 puts most of the map in one bin)
   const long long* a = abar + (size_t)bh * dm.ntri;
-  for (long long e = begin + tid; e < end; e += kThreads) {
-    const long long v = a[e];
-    if ((v >> hi) == (prefix >> hi)) {
-      const int dg = (int)((v >> shift) & ((1 << width) - 1));
-      atomicAdd(&cnt[dg], 1u);
-      atomicAdd(&mass[dg], (unsigned long long)v);
+  constexpr int kRun = 16;
+  int cur = -1;
+  unsigned ccnt = 0;
+  unsigned long long cmass = 0;
+  auto add = [&](long long v) {
+    if ((v >> hi) != (prefix >> hi)) return;
+    const int dg = (int)((v >> shift) & ((1 << width) - 1));
+    if (dg != cur) {
+      if (ccnt) {
+        atomicAdd(&cnt[cur], ccnt);
+        atomicAdd(&mass[cur], cmass);
+      }
+      cur = dg, ccnt = 0, cmass = 0;
     }
+    ++ccnt;
+    cmass += (unsigned long long)v;
+  };
+  for (long long e0 = begin + (long long)tid * kRun; e0 < end; e0 += (long long)kThreads * kRun) {
+    if (e0 + kRun <= end && (((size_t)(a + e0)) & 15) == 0) {
+      longlong2 w[kRun / 2];
+#pragma unroll
+      for (int j = 0; j < kRun / 2; ++j) w[j] = reinterpret_cast<const longlong2*>(a + e0)[j];
+#pragma unroll
+      for (int j = 0; j < kRun / 2; ++j) add(w[j].x), add(w[j].y);
+    } else {
+      for (long long e = e0; e < end && e < e0 + kRun; ++e) add(a[e]);
+    }
+  }
+  if (ccnt) {
+    atomicAdd(&cnt[cur], ccnt);
+    atomicAdd(&mass[cur], cmass);
   }
   __syncthreads();
   unsigned long long* h = hist + ((size_t)bh * 4 + pass) * kHistBins * 2;
@@ -563,7 +600,9 @@ __global__ __launch_bounds__(kThreads) void pe_write_kernel(Dims dm, IndexOut io
 template <typename T>
 void launch_pool(const Dims& dm, const void* q, const void* k, const IndexOut& io, float* qbar,
                  float* kbar, hipStream_t st) {
-  pe_pool_kernel<T><<<dim3(dm.nb, dm.bh + dm.bkv), dm.d, 0, st>>>(
+  const int upb = 256 / (dm.d / 8);  // units per workgroup
+  const long long units = (long long)(dm.bh + dm.bkv) * dm.nb;
+  pe_pool_kernel<T><<<(unsigned)((units + upb - 1) / upb), 256, 0, st>>>(
       dm, static_cast<const T*>(q), static_cast<const T*>(k), io, qbar, kbar);
 }
 
