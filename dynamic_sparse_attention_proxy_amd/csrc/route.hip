@@ -60,13 +60,39 @@ __global__ __launch_bounds__(kThreads) void proxy_scores_kernel(const T* __restr
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = 0.0f;
 
+  // Staging: a 32-dim chunk of Q and K is B x 4 pieces of 8 dims; piece g has
+  // row g % B and dims 8 (g / B) ..; it is read with one 16-byte (bf16) load,
+  // held in registers while the previous chunk is computed, and stored
+  // transposed (dim-major) so that the lanes of a wave write consecutive rows.
+  constexpr int kPieces = B * KC / 8 / kThreads;  // pieces per thread and operand
+  float qv[kPieces][8], kv[kPieces][8];
+  auto fetch = [&](int dc) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int g = tid + kThreads * i, r = g % B, d8 = (g / B) * 8;
+      if (r < dm.qrows) load8(qbase + (size_t)r * D + dc + d8, qv[i]);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[i][j] = 0.0f;
+      if (r < krows) load8(kbase + (size_t)r * D + dc + d8, kv[i]);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kv[i][j] = 0.0f;
+    }
+  };
+  fetch(0);
   for (int dc = 0; dc < D; dc += KC) {
-    for (int e = tid; e < B * KC; e += kThreads) {
-      const int r = e / KC, kk = e % KC;
-      Qs[kk * LD + r] = (r < dm.qrows) ? load_f32(qbase + (size_t)r * D + dc + kk) : 0.0f;
-      Ks[kk * LD + r] = (r < krows) ? load_f32(kbase + (size_t)r * D + dc + kk) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int g = tid + kThreads * i, r = g % B, d8 = (g / B) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        Qs[(d8 + j) * LD + r] = qv[i][j];
+        Ks[(d8 + j) * LD + r] = kv[i][j];
+      }
     }
     __syncthreads();
+    if (dc + KC < D) fetch(dc + KC);
 #pragma unroll 4
     for (int kk = 0; kk < KC; ++kk) {
       float a[TM], bb[TM];
