@@ -64,6 +64,39 @@ def tile_counts(bufs, spec):
     return out
 
 
+def useful_pair_density(bufs, spec):
+    """Allowed (query, key) pairs of the selected index sets / causal pairs (host, exact;
+    n a multiple of the block size)."""
+    import numpy as np
+    B, n, nb = spec.block, spec.seq_len, spec.num_blocks
+    if n % B:
+        return None
+    route = bufs.route.cpu().numpy()
+    cnt = bufs.vs_count.cpu().numpy()
+    vv = bufs.vs_vertical.cpu().numpy()
+    ss = bufs.vs_slash.cpu().numpy()
+    rp = bufs.pe_rowptr.cpu().numpy()
+    low, up, full = B * (B + 1) // 2, B * (B - 1) // 2, B * B
+    delta = np.arange(nb)[:, None] - np.arange(nb)[None, :]
+    causal = delta >= 0
+    total = 0
+    for h in range(len(route)):
+        if route[h]:
+            inv = np.zeros(nb, bool)
+            inv[vv[h, : cnt[h, 0]]] = True
+            ins = np.zeros(nb + 1, bool)
+            ins[ss[h, : cnt[h, 1]]] = True
+            d = np.clip(delta, 0, nb)
+            s_lo = ins[d]
+            s_up = (delta >= 1) & ins[np.clip(delta - 1, 0, nb)]
+            col = inv[None, :]
+            per = np.where(col, np.where(delta == 0, low, full), s_lo * low + s_up * up)
+            total += int(per[causal].sum())
+        else:
+            total += int(rp[h, -1] - nb) * full + nb * low  # off-diagonal tiles full, diagonal causal
+    return total / (len(route) * n * (n + 1) / 2)
+
+
 def time_calls(fn, reps, stream):
     import torch
     start = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
@@ -312,6 +345,7 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
         res["dense_ms"] = sum(time_calls(lambda: crisp.dense_prefill(spec, q, k, v, od, bufs, bo, bv), dense_reps,
                                          stream)) / dense_reps
     res["tiles"] = tile_counts(bufs, spec)
+    res["pair_density"] = useful_pair_density(bufs, spec)
     # the divergence router on the same proxy: its extra cost and its agreement with C_struct
     rj = torch.zeros(spec.heads, dtype=torch.uint8, device="cuda")
     jj = torch.zeros(spec.heads, dtype=torch.int64, device="cuda")
@@ -386,6 +420,8 @@ def main():
         "tokens_per_s": round(wl.n / (total_ms * 1e-3), 1),
         "stage_ms": {kk: round(vv, 3) for kk, vv in st.items()},
         "tile_density": round(tiles / causal_tiles, 4),
+        "useful_pair_density": None if r["pair_density"] is None else round(r["pair_density"], 4),
+        "route_select_share_of_attention": round((st["route"] + st["select"]) / st["attention"], 4),
         "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel (crisp_sparse_prefill launch)",
                      "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
