@@ -32,8 +32,15 @@ def log(*a):
 
 
 def source_hash(path=ATTN_SOURCE) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention source with comments and blank lines removed, so that
+    a recorded traffic figure stays attached to the code it was measured on."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def tile_counts(bufs, spec):

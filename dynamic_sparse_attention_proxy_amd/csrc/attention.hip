@@ -1,8 +1,8 @@
 // Sparse and dense causal prefill attention (CRISP summary page, "Algorithm
 // Overview", Alg. 1: attention over the selected index set).
 //
-// Work item = (head, query block of B rows).  Its key tiles (key block kb,
-// mask mode) come from a per-item list (sparse) or are 0..qb (dense):
+// The key tiles of a (head, query block qb) -- key block kb and a mask mode --
+// come from the index sets (sparse) or are 0..qb (dense):
 //   VS head : kb in V (whole tile), kb = qb - s for s in S (lower triangle
 //             r >= c of the tile: offsets in block s), kb = qb - s - 1
 //             (upper triangle r < c: the same offset block from the tile
@@ -11,14 +11,19 @@
 //   PE head : the CSR row of query block qb.
 //   Every tile is intersected with causality (diagonal tile: r >= c).
 //
-// bf16, d = 128, B = 128: matrix-core engine.  Each of the 4 waves owns 32
-// query rows.  S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 so that a
-// lane holds one query's scores: the softmax max / sum need one cross-half
-// exchange only, and the probabilities are already laid out as the B operand
-// of O^T = V^T P^T (the key order inside each 32-key group is permuted on the
-// K side to make that layout line up).  K is staged in LDS row-major, V is
-// transposed in registers (8 x 8 bf16 blocks) while being staged, so every
-// LDS read feeding a matrix instruction is one 16-byte vector.
+// bf16, d = 128, B = 128: matrix-core engine (attn_mfma_kernel).  A persistent
+// workgroup per CU takes work items (KV head, pair of its query heads, query
+// block) from per-XCD queues; its 8 waves each own 32 query rows of one of the
+// two heads, so every K / V^T tile brought into LDS serves 256 query rows.
+// S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 so that a lane holds
+// one query's scores (the softmax needs one cross-half exchange at most), and
+// the probabilities are already laid out as the B operand of O^T = V^T P^T
+// (the key order inside each 32-key group is permuted on the K side to make
+// that layout line up).  V^T is written to the workspace once per call, so
+// both tiles reach LDS by direct global-to-LDS loads and every LDS read that
+// feeds a matrix instruction is one 16-byte vector.
+// Other shapes (fp32, d = 64, B = 64): attn_generic_kernel, one thread per
+// query row on the fp32 vector ALU, same tile lists and masks.
 #include <type_traits>
 
 #include "common.h"
