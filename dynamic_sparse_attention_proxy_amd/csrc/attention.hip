@@ -497,6 +497,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
           soft(a);
         }
         vload(3);
+        pinf(vf);
         pv(3);
       }
     };
