@@ -140,11 +140,6 @@ __device__ __forceinline__ int key_perm(int rho) {
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-__device__ __forceinline__ unsigned uniform(unsigned x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ const unsigned char* uniform(const unsigned char* p) {
-  const unsigned long long v = (unsigned long long)p;
-  return (const unsigned char*)(((unsigned long long)uniform((unsigned)(v >> 32)) << 32) | uniform((unsigned)v));
-}
 // lds_wave + kBufImm addresses the slot: lds_wave is a per-wave scalar, the
 // constant part is encoded in the instruction stream.
 template <unsigned kLdsConst>
