@@ -129,6 +129,36 @@ __device__ __forceinline__ long long wave_sum_i64(long long v) {
   return v;
 }
 
+// Sum / max over one workgroup (every thread gets the result); red holds one
+// slot per wave.  The trailing barrier lets the caller reuse red at once.
+__device__ __forceinline__ long long block_sum_i64(long long v, long long* red) {
+  v = wave_sum_i64(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  long long s = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ float block_max_f32(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = red[w] > r ? red[w] : r;
+  __syncthreads();
+  return r;
+}
+
 // Ascending compaction of flags over one block of threads.  Returns the
 // position of this thread's element (valid if flag) and the block total.
 __device__ __forceinline__ int block_compact(bool flag, int* wave_cnt, int* total) {

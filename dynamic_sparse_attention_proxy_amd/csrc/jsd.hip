@@ -123,34 +123,6 @@ __device__ __forceinline__ double log_crisp(double x) {
 
 constexpr int kFinThreads = 1024;
 
-__device__ __forceinline__ long long fin_sum_i64(long long v, long long* red) {
-  v = wave_sum_i64(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  long long s = 0;
-  for (int w = 0; w < kFinThreads / 64; ++w) s += red[w];
-  __syncthreads();
-  return s;
-}
-
-__device__ __forceinline__ float fin_max_f32(float v, float* red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < kFinThreads / 64; ++w) r = red[w] > r ? red[w] : r;
-  __syncthreads();
-  return r;
-}
-
 // Softmax of the pooled row in fixed point, the divergence from p^v / T and
 // the routing decision; one workgroup per query head.
 __global__ __launch_bounds__(kFinThreads) void jsd_finish_kernel(Dims dm, unsigned tau_num, unsigned tau_den,
@@ -168,10 +140,10 @@ __global__ __launch_bounds__(kFinThreads) void jsd_finish_kernel(Dims dm, unsign
   long long* a = abar + (size_t)bh * nb;
   float m = -__builtin_inff();
   for (int b = tid; b < nb; b += kFinThreads) m = z[b] > m ? z[b] : m;
-  m = fin_max_f32(m, redf);
+  m = block_max_f32(m, redf);
   long long L = 0;
   for (int b = tid; b < nb; b += kFinThreads) L += fix_rne(exp_crisp(z[b] - m));
-  L = fin_sum_i64(L, redi);
+  L = block_sum_i64(L, redi);
   const float l = fix_to_float(L);
   long long ta = 0;
   for (int b = tid; b < nb; b += kFinThreads) {
@@ -180,7 +152,7 @@ __global__ __launch_bounds__(kFinThreads) void jsd_finish_kernel(Dims dm, unsign
     if (pooled) pooled[(size_t)bh * nb + b] = aq;
     ta += aq;
   }
-  ta = fin_sum_i64(ta, redi);  // the barrier inside also orders the writes of a[] before the reads below
+  ta = block_sum_i64(ta, redi);  // the barrier inside also orders the writes of a[] before the reads below
   const double dT = (double)mass_total[bh], dTa = (double)ta;
   const long long* pv = mass_v + (size_t)bh * nb;
   long long J = 0;
@@ -193,7 +165,7 @@ __global__ __launch_bounds__(kFinThreads) void jsd_finish_kernel(Dims dm, unsign
     const double t = tp + tq;
     J += (long long)__builtin_rint(__builtin_ldexp(t, kJsdShift));
   }
-  J = fin_sum_i64(J, redi);
+  J = block_sum_i64(J, redi);
   if (tid == 0) {
     jsd[bh] = J;
     // JSD = J 2^-53 >= tau_num / tau_den, as integers

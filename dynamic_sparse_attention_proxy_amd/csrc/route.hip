@@ -276,17 +276,6 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
   }
 }
 
-__device__ __forceinline__ long long block_sum_i64(long long v, long long* red) {
-  v = wave_sum_i64(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  long long s = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
-  return s;
-}
-
 __global__ __launch_bounds__(kThreads) void route_finish_kernel(Dims dm, RouteArgs ra,
                                                                 const long long* __restrict__ part,
                                                                 IndexOut io) {

@@ -28,18 +28,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ long long block_sum_i64(long long v, long long* red) {
-  v = wave_sum_i64(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  long long s = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
-  __syncthreads();
-  return s;
-}
-
 __global__ __launch_bounds__(kThreads) void vs_select_kernel(Dims dm, SelectArgs sa, IndexOut io) {
   __shared__ int wave_cnt[4];
   const int bh = blockIdx.x, tid = threadIdx.x, nb = dm.nb;
@@ -261,22 +249,6 @@ __global__ __launch_bounds__(kThreads) void pe_scores_kernel(Dims dm, IndexOut i
       if (kb <= qb) zbar[((size_t)bh * dm.nb + qb) * dm.nb + kb] = acc[i][j] * c;
     }
   }
-}
-
-__device__ __forceinline__ float block_max_f32(float v, float* red) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    float o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = red[w] > r ? red[w] : r;
-  __syncthreads();
-  return r;
 }
 
 // Row softmax of the pooled map in fixed point: Abar_q row, row total.
