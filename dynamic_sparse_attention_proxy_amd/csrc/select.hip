@@ -251,32 +251,41 @@ __global__ __launch_bounds__(kThreads) void pe_scores_kernel(Dims dm, IndexOut i
   }
 }
 
-// Row softmax of the pooled map in fixed point: Abar_q row, row total.
+// Row softmax of the pooled map in fixed point: Abar_q row, row total.  One
+// wave per query block (four rows per workgroup), so every reduction is a
+// wave reduction; rows are assigned longest first (row nb - 1 - r).
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
 __global__ __launch_bounds__(kThreads) void pe_rowsoft_kernel(Dims dm, IndexOut io,
                                                               const float* __restrict__ zbar,
                                                               long long* __restrict__ abar,
                                                               long long* __restrict__ rowtot) {
-  __shared__ float redf[4];
-  __shared__ long long redi[4];
-  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  if (io.route[bh]) return;
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int qb = dm.nb - 1 - (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
+  if (qb < 0 || io.route[bh]) return;
   const float* z = zbar + ((size_t)bh * dm.nb + qb) * dm.nb;
   float m = -__builtin_inff();
-  for (int kb = tid; kb <= qb; kb += kThreads) m = z[kb] > m ? z[kb] : m;
-  m = block_max_f32(m, redf);
+  for (int kb = lane; kb <= qb; kb += 64) m = z[kb] > m ? z[kb] : m;
+  m = wave_max_f32(m);
   long long L = 0;
-  for (int kb = tid; kb <= qb; kb += kThreads) L += fix_rne(exp_crisp(z[kb] - m));
-  L = block_sum_i64(L, redi);
+  for (int kb = lane; kb <= qb; kb += 64) L += fix_rne(exp_crisp(z[kb] - m));
+  L = wave_sum_i64(L);
   const float l = fix_to_float(L);
   long long* out = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
   long long tot = 0;
-  for (int kb = tid; kb <= qb; kb += kThreads) {
+  for (int kb = lane; kb <= qb; kb += 64) {
     const long long aq = fix_rne(exp_crisp(z[kb] - m) / l);
     out[kb] = aq;
     tot += aq;
   }
-  tot = block_sum_i64(tot, redi);
-  if (tid == 0) rowtot[(size_t)bh * dm.nb + qb] = tot;
+  tot = wave_sum_i64(tot);
+  if (lane == 0) rowtot[(size_t)bh * dm.nb + qb] = tot;
 }
 
 // Radix-select state per head (int64 slots):
@@ -434,14 +443,15 @@ __global__ __launch_bounds__(kThreads) void pe_count_kernel(Dims dm, IndexOut io
                                                             const long long* __restrict__ abar,
                                                             const long long* __restrict__ state,
                                                             int* __restrict__ gtcnt, int* __restrict__ tiecnt) {
-  __shared__ int red[8];
-  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  if (io.route[bh]) return;
+  // one wave per query block, longest rows first
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int qb = dm.nb - 1 - (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
+  if (qb < 0 || io.route[bh]) return;
   const long long vstar = state[(size_t)bh * 8 + 2];
   const long long* a = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
   int gt = 0, tie = 0;
   if (vstar >= 0 && vstar != 0x7fffffffffffffffLL)
-    for (int kb = tid; kb <= qb; kb += kThreads) {
+    for (int kb = lane; kb <= qb; kb += 64) {
       gt += a[kb] > vstar;
       tie += a[kb] == vstar;
     }
@@ -450,14 +460,11 @@ __global__ __launch_bounds__(kThreads) void pe_count_kernel(Dims dm, IndexOut io
     gt += __shfl_xor(gt, m);
     tie += __shfl_xor(tie, m);
   }
-  if ((tid & 63) == 0) red[tid >> 6] = gt, red[4 + (tid >> 6)] = tie;
-  __syncthreads();
-  if (tid == 0) {
-    gtcnt[(size_t)bh * dm.nb + qb] = red[0] + red[1] + red[2] + red[3];
-    tiecnt[(size_t)bh * dm.nb + qb] = red[4] + red[5] + red[6] + red[7];
+  if (lane == 0) {
+    gtcnt[(size_t)bh * dm.nb + qb] = gt;
+    tiecnt[(size_t)bh * dm.nb + qb] = tie;
   }
 }
-
 // Row pointers: exclusive scans over query blocks of the tie counts and the
 // row sizes (values above v*, the first ties, plus the diagonal if not in).
 __global__ __launch_bounds__(1024) void pe_scan_kernel(Dims dm, IndexOut io,
@@ -543,32 +550,32 @@ __global__ __launch_bounds__(kThreads) void pe_write_kernel(Dims dm, IndexOut io
                                                             const long long* __restrict__ abar,
                                                             const long long* __restrict__ state,
                                                             const int* __restrict__ tiepre) {
-  __shared__ int wave_cnt[4];
-  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  if (io.route[bh]) return;
+  // one wave per query block, longest rows first; ascending compaction by ballots
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int qb = dm.nb - 1 - (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
+  if (qb < 0 || io.route[bh]) return;
   const long long* st = state + (size_t)bh * 8;
   const long long vstar = st[2], rties = st[3];
   const bool all = vstar < 0;
   const long long* a = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
   int* out = io.pe_col + (size_t)bh * io.pe_cap + io.pe_rowptr[(size_t)bh * (dm.nb + 1) + qb];
   long long tcur = all ? 0 : tiepre[(size_t)bh * dm.nb + qb];
+  const unsigned long long below = (1ull << lane) - 1ull;
   int cnt = 0;
-  for (int base = 0; base <= qb; base += kThreads) {
-    const int kb = base + tid;
+  for (int base = 0; base <= qb; base += 64) {
+    const int kb = base + lane;
     const bool in = kb <= qb;
     const long long v = (in && !all) ? a[kb] : 0;
     const bool tie = in && !all && v == vstar;
-    int ntie;
-    const int tpos = block_compact(tie, wave_cnt, &ntie);
-    bool flag = in && (all || v > vstar || kb == qb || (tie && tcur + tpos < rties));
-    tcur += ntie;
-    int tot;
-    const int pos = block_compact(flag, wave_cnt, &tot);
-    if (flag) out[cnt + pos] = kb;
-    cnt += tot;
+    const unsigned long long tmask = __ballot(tie);
+    const int tpos = __popcll(tmask & below);
+    const bool flag = in && (all || v > vstar || kb == qb || (tie && tcur + tpos < rties));
+    tcur += __popcll(tmask);
+    const unsigned long long fmask = __ballot(flag);
+    if (flag) out[cnt + __popcll(fmask & below)] = kb;
+    cnt += __popcll(fmask);
   }
 }
-
 template <typename T>
 void launch_pool(const Dims& dm, const void* q, const void* k, const IndexOut& io, float* qbar,
                  float* kbar, hipStream_t st) {
@@ -582,6 +589,7 @@ void launch_pool(const Dims& dm, const void* q, const void* k, const IndexOut& i
 
 hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, const void* k,
                          const SelectScratch& ws, const IndexOut& io, hipStream_t st) {
+  const dim3 rows((dm.nb + kThreads / 64 - 1) / (kThreads / 64), dm.bh);  // one wave per query block
   vs_select_kernel<<<dm.bh, kThreads, 0, st>>>(dm, sa, io);
   if (sa.cumulative) vs_cumulative_kernel<<<dm.bh * 2, kCumThreads, 0, st>>>(dm, sa, io);
   if (!sa.keep_all) {
@@ -594,7 +602,7 @@ hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, co
       pe_scores_kernel<128><<<dim3(nt, nt, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
     else
       pe_scores_kernel<64><<<dim3(nt, nt, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
-    pe_rowsoft_kernel<<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, io, ws.zbar, ws.abar, ws.rowtot);
+    pe_rowsoft_kernel<<<rows, kThreads, 0, st>>>(dm, io, ws.zbar, ws.abar, ws.rowtot);
   }
   pe_radix_init_kernel<<<dm.bh, kThreads, 0, st>>>(dm, sa, io, ws.rowtot, ws.hist, ws.state);
   if (!sa.keep_all) {
@@ -605,11 +613,10 @@ hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, co
                                                                         ws.state, chunk);
       pe_radix_scan_kernel<<<dm.bh, kThreads, 0, st>>>(dm, io, pass, ws.hist, ws.state);
     }
-    pe_count_kernel<<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.gtcnt,
-                                                             ws.tiecnt);
+    pe_count_kernel<<<rows, kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.gtcnt, ws.tiecnt);
   }
   pe_scan_kernel<<<dm.bh, 1024, 0, st>>>(dm, io, ws.abar, ws.state, ws.gtcnt, ws.tiecnt, ws.tiepre);
-  pe_write_kernel<<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.tiepre);
+  pe_write_kernel<<<rows, kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.tiepre);
   return hipGetLastError();
 }
 
