@@ -103,6 +103,12 @@ __device__ __forceinline__ long long fix_rne(float v) {
   return (long long)__builtin_rintf(__builtin_ldexpf(v, kFixShift));
 }
 
+// The same value as an integer-valued fp32 (<= 2^40): sums of up to 2^13 such
+// terms are exact in fp64, which is cheaper to accumulate than int64.
+__device__ __forceinline__ float fix_rne_f(float v) {
+  return __builtin_rintf(__builtin_ldexpf(v, kFixShift));
+}
+
 // fl32(L) * 2^-40 (int64 -> fp32 rounds to nearest even).
 __device__ __forceinline__ float fix_to_float(long long L) {
   return __builtin_ldexpf((float)L, -kFixShift);

@@ -192,16 +192,32 @@ __global__ __launch_bounds__(kThreads) void proxy_rowsum_kernel(Dims dm, const f
   long long acc[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 4; ++e) m[e] = ordered_to_float(m_enc[bh * B + rg * 4 + e]);
+  if (kb < dm.nb - 1 && dm.qrows == B) {
+    // every (row, key) of the tile is valid: integer-valued terms summed in fp64
+    // (at most IT terms of <= 2^40 each, exact)
+    double accd[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
-  for (int it = 0; it < Lay::IT; ++it) {
-    const int c = cp + Lay::CP * it;
-    const int jj = kb * B + c;
-    const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
-    const float z[4] = {z4.x, z4.y, z4.z, z4.w};
+    for (int it = 0; it < Lay::IT; ++it) {
+      const int c = cp + Lay::CP * it;
+      const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
+      const float z[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = rg * 4 + e;
-      if (r < dm.qrows && jj <= dm.q0 + r) acc[e] += fix_rne(exp_crisp(z[e] - m[e]));
+      for (int e = 0; e < 4; ++e) accd[e] += (double)fix_rne_f(exp_crisp(z[e] - m[e]));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = (long long)accd[e];
+  } else {
+#pragma unroll 4
+    for (int it = 0; it < Lay::IT; ++it) {
+      const int c = cp + Lay::CP * it;
+      const int jj = kb * B + c;
+      const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
+      const float z[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rg * 4 + e;
+        if (r < dm.qrows && jj <= dm.q0 + r) acc[e] += fix_rne(exp_crisp(z[e] - m[e]));
+      }
     }
   }
 #pragma unroll
@@ -232,6 +248,27 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
     l[e] = fix_to_float(L[bh * B + rg * 4 + e]);
   }
   long long lo = 0, up = 0, an = 0;
+  const bool plain = kb < dm.nb - 1 && dm.qrows == B && kb * B >= ra.w_sink &&
+                     dm.q0 - (kb * B + B - 1) >= ra.w_local;
+  if (plain) {
+    // every (row, key) is valid and none is an anchor: integer-valued terms summed
+    // in fp64 (at most 4 IT terms of <= 2^40 each, exact); upper = all - lower
+    double alld = 0.0, lod = 0.0;
+#pragma unroll 4
+    for (int it = 0; it < Lay::IT; ++it) {
+      const int c = cp + Lay::CP * it;
+      const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
+      const float z[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double aq = (double)fix_rne_f(exp_crisp(z[e] - m[e]) / l[e]);
+        alld += aq;
+        lod += rg * 4 + e >= c ? aq : 0.0;
+      }
+    }
+    lo = (long long)lod;
+    up = (long long)alld - lo;
+  } else
 #pragma unroll 4
   for (int it = 0; it < Lay::IT; ++it) {
     const int c = cp + Lay::CP * it;
