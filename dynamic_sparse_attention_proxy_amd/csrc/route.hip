@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
     // every (row, key) is valid and none is an anchor: integer-valued terms summed
     // in fp64 (at most 4 IT terms of <= 2^40 each, exact); upper = all - lower
     double alld = 0.0, lod = 0.0;
-#pragma unroll 4
+#pragma unroll 8
     for (int it = 0; it < Lay::IT; ++it) {
       const int c = cp + Lay::CP * it;
       const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
