@@ -229,7 +229,7 @@ def _variant_stats(wl, X, **overrides):
     return row
 
 
-def selection_sweep(names=("llama_32k", "llama_128k", "llama_512k")):
+def selection_sweep(names=("llama_32k", "llama_128k", "qwen_128k", "llama_512k")):
     """Selected budget and sparse-attention time of the noise-floor rule against the
     cumulative-coverage rule, over sequence length (VS heads; PE heads are the same)."""
     import torch
@@ -378,7 +378,7 @@ def main():
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K speedup side measurement")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--selection-sweep", action="store_true",
-                    help="add the noise-floor vs cumulative-coverage budget over 32K/128K/512K")
+                    help="add the noise-floor vs cumulative-coverage budget over 32K/128K/512K and the Qwen-shaped 128K layer")
     ap.add_argument("--param-sweep", action="store_true",
                     help="add the alpha in {1, 5/4, 3/2} and gamma in {19/20, 97/100} variants at 128K/512K")
     args = ap.parse_args()
