@@ -91,6 +91,12 @@ def _check_jsd(wl, I, X, spec, bufs, ref):
     assert np.array_equal(p_gpu.cpu().numpy(), want["abar"]), "pooled estimate"
     assert np.array_equal(j_gpu.cpu().numpy(), want["jsd"]), (j_gpu.cpu().numpy()[:4], want["jsd"][:4])
     assert np.array_equal(r_gpu.cpu().numpy(), want["route"])
+    # the pooled estimate is an optional output: without it the router gives the same bits
+    r2 = torch.zeros_like(r_gpu)
+    j2 = torch.zeros_like(j_gpu)
+    crisp.route_jsd(spec, X.q, X.k, bufs, r2, j2, JSD_TAU, None)
+    torch.cuda.synchronize()
+    assert torch.equal(r2, r_gpu) and torch.equal(j2, j_gpu)
     return want
 
 
