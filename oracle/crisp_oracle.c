@@ -19,7 +19,7 @@
  *   Motivation / Key Contributions: the Jensen-Shannon divergence router that
  *            C_struct replaces (pooled estimate against per-query estimate).
  *
- * Precision (the pages leave it open; these readings are stated in the design doc):
+ * Precision (the pages leave it open; these are the readings taken here):
  *   - proxy scores are fp32: acc = fmaf(q[k], key[k], acc) for k ascending,
  *     z = fl(acc * c) with c = fl32(1/sqrt(d)), then z = fl(z + bias);
  *   - exp_crisp below (Cody-Waite reduction, degree-7 Taylor, all fp32);
