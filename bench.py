@@ -270,6 +270,30 @@ def param_sweep(names=("llama_128k", "llama_512k")):
     return out
 
 
+def per_config(names=("tiny", "llama_32k", "llama_128k", "qwen_128k", "llama_512k")):
+    """Stage times, own dense time, speedup and densities of every workload (3 steps)."""
+    import torch
+
+    import synth
+    out = {}
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        r = measure(wl, 3, 1)
+        st = r["stage_ms"]
+        tot = st["route"] + st["select"] + st["attention"]
+        nb = (wl.n + wl.block - 1) // wl.block
+        row = {"sparse_ms": round(tot, 3), "stage_ms": {k: round(v, 3) for k, v in st.items()},
+               "tokens_per_s": round(wl.n / (tot * 1e-3), 1), "dense_ms": round(r["dense_ms"], 3),
+               "speedup_vs_dense": round(r["dense_ms"] / tot, 3),
+               "tile_density": round(sum(r["tiles"]) / (wl.batch * wl.hq * nb * (nb + 1) / 2), 4),
+               "useful_pair_density": None if r["pair_density"] is None else round(r["pair_density"], 4)}
+        out[name] = row
+        log(f"per-config {name}: {row}")
+        del r
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(gib: float = 4.0):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -379,6 +403,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--selection-sweep", action="store_true",
                     help="add the noise-floor vs cumulative-coverage budget over 32K/128K/512K and the Qwen-shaped 128K layer")
+    ap.add_argument("--per-config", action="store_true",
+                    help="add stage times, dense time, speedup and densities for every workload")
     ap.add_argument("--param-sweep", action="store_true",
                     help="add the alpha in {1, 5/4, 3/2} and gamma in {19/20, 97/100} variants at 128K/512K")
     args = ap.parse_args()
@@ -456,6 +482,8 @@ def main():
         out["selection_sweep"] = selection_sweep()
     if args.param_sweep:
         out["param_sweep"] = param_sweep()
+    if args.per_config:
+        out["per_config"] = per_config()
     if not args.no_cpu_baseline:
         t = time.time()
         out["cpu_baseline"] = cpu_baseline(wl, r["I"])
