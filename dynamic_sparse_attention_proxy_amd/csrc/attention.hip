@@ -617,18 +617,24 @@ __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, Ind
 
 // ----------------------------------------------------------- vector engine --
 // One thread per query row; keys staged 32 at a time through LDS in fp32.
-template <typename T, int D>
-__global__ __launch_bounds__(128) void attn_generic_kernel(const T* __restrict__ q, const T* __restrict__ k,
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, T* __restrict__ o,
                                                            Dims dm, BiasArgs bias, const int* __restrict__ tiles,
                                                            const int* __restrict__ tile_cnt, int dense) {
+  // G groups of B threads split the key tiles of one (head, query block) item
+  // (group g takes tiles g, g + G, ...); each thread keeps one query row's
+  // running max, sum and output, and the groups' partial results are merged
+  // at the end in group order.
   constexpr int KCH = 32;
-  __shared__ float Kc[KCH * D];
-  __shared__ float Vc[KCH * D];
+  __shared__ float Kc[G][KCH * D];
+  __shared__ float Vc[G][KCH * D];
+  __shared__ float Cm[G > 1 ? 128 : 1], Cl[G > 1 ? 128 : 1];
+  __shared__ float Ca[G > 1 ? 128 * D : 1];
   int qb, bh;
   work_item(dm, blockIdx.x, &qb, &bh);
   const int B = dm.B;
-  const int r = threadIdx.x;
+  const int g = threadIdx.x / B, r = threadIdx.x % B;
   const int i = qb * B + r;
   const int b = bh / dm.hq;
   const int kvh = b * dm.hkv + (bh % dm.hq) / dm.group;
@@ -640,29 +646,42 @@ __global__ __launch_bounds__(128) void attn_generic_kernel(const T* __restrict__
     qv[t] = i < dm.n ? load_f32(q + ((size_t)bh * dm.n + i) * D + t) : 0.0f;
     acc[t] = 0.0f;
   }
+  int boff[8];
+  float bval[8];
+#pragma unroll
+  for (int t2 = 0; t2 < 8; ++t2) {
+    boff[t2] = t2 < bias.count ? bias.offsets[(size_t)bh * bias.count + t2] : -1;
+    bval[t2] = t2 < bias.count ? bias.values[(size_t)bh * bias.count + t2] : 0.0f;
+  }
   const float c = (float)(1.0 / __builtin_sqrt((double)D));
   float m = -__builtin_inff(), l = 0.0f;
   const int ntile = dense ? qb + 1 : tile_cnt[(size_t)bh * dm.nb + qb];
   const int* tl = dense ? nullptr : tiles + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
-  for (int t = 0; t < ntile; ++t) {
-    int kb, mode;
-    if (dense) {
-      kb = t;
-      mode = kModeFull;
-    } else {
-      kb = tl[t] & 0x0fffffff;
-      mode = tl[t] >> 28;
+  const int rounds = (ntile + G - 1) / G;  // every group runs the same number of rounds (block barriers)
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int t = rd * G + g;
+    const bool active = t < ntile;
+    int kb = 0, mode = kModeFull;
+    if (active) {
+      if (dense) {
+        kb = t;
+      } else {
+        kb = tl[t] & 0x0fffffff;
+        mode = tl[t] >> 28;
+      }
     }
     const bool diag = kb == qb;
     for (int sub = 0; sub < B; sub += KCH) {
       __syncthreads();
-      for (int e = threadIdx.x; e < KCH * D; e += blockDim.x) {
-        const int kk = e / D, dd = e % D;
-        const int key = kb * B + sub + kk;
-        Kc[e] = key < dm.n ? load_f32(kp + (size_t)key * D + dd) : 0.0f;
-        Vc[e] = key < dm.n ? load_f32(vp + (size_t)key * D + dd) : 0.0f;
-      }
+      if (active)
+        for (int e = r; e < KCH * D; e += B) {
+          const int kk = e / D, dd = e % D;
+          const int key = kb * B + sub + kk;
+          Kc[g][e] = key < dm.n ? load_f32(kp + (size_t)key * D + dd) : 0.0f;
+          Vc[g][e] = key < dm.n ? load_f32(vp + (size_t)key * D + dd) : 0.0f;
+        }
       __syncthreads();
+      if (!active) continue;
       float s[KCH];
       float cmax = -__builtin_inff();
       for (int kk = 0; kk < KCH; ++kk) {
@@ -670,10 +689,11 @@ __global__ __launch_bounds__(128) void attn_generic_kernel(const T* __restrict__
         const int j = kb * B + cc;
         float dot = 0.0f;
 #pragma unroll
-        for (int t2 = 0; t2 < D; ++t2) dot = __builtin_fmaf(qv[t2], Kc[kk * D + t2], dot);
+        for (int t2 = 0; t2 < D; ++t2) dot = __builtin_fmaf(qv[t2], Kc[g][kk * D + t2], dot);
         float z = dot * c;
-        for (int t2 = 0; t2 < bias.count; ++t2)
-          if (bias.offsets[(size_t)bh * bias.count + t2] == i - j) z += bias.values[(size_t)bh * bias.count + t2];
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2)
+          if (boff[t2] == i - j) z += bval[t2];
         const bool ok = j < dm.n && j <= i && tile_keep(mode, diag, r, cc);
         s[kk] = ok ? z : -__builtin_inff();
         cmax = s[kk] > cmax ? s[kk] : cmax;
@@ -688,12 +708,34 @@ __global__ __launch_bounds__(128) void attn_generic_kernel(const T* __restrict__
         const float p = expf(s[kk] - m_new);
         l += p;
 #pragma unroll
-        for (int t2 = 0; t2 < D; ++t2) acc[t2] = __builtin_fmaf(p, Vc[kk * D + t2], acc[t2]);
+        for (int t2 = 0; t2 < D; ++t2) acc[t2] = __builtin_fmaf(p, Vc[g][kk * D + t2], acc[t2]);
       }
       m = m_new;
     }
   }
-  if (i < dm.n) {
+  // merge the groups' partial results into group 0, in group order
+  for (int w = 1; w < G; ++w) {
+    __syncthreads();
+    if (g == w) {
+      Cm[r] = m;
+      Cl[r] = l;
+#pragma unroll
+      for (int t2 = 0; t2 < D; ++t2) Ca[r * D + t2] = acc[t2];
+    }
+    __syncthreads();
+    if (g == 0) {
+      const float mw = Cm[r];
+      const float m_new = mw > m ? mw : m;
+      if (m_new != -__builtin_inff()) {
+        const float a0 = expf(m - m_new), a1 = expf(mw - m_new);
+        l = l * a0 + Cl[r] * a1;
+#pragma unroll
+        for (int t2 = 0; t2 < D; ++t2) acc[t2] = acc[t2] * a0 + Ca[r * D + t2] * a1;
+        m = m_new;
+      }
+    }
+  }
+  if (g == 0 && i < dm.n) {
     const float inv = 1.0f / l;
     T* op = o + ((size_t)bh * dm.n + i) * D;
 #pragma unroll
@@ -713,9 +755,22 @@ template <typename T, int D>
 void launch_generic(const Dims& dm, const BiasArgs& bias, const void* q, const void* k, const void* v,
                     void* o, const int* tiles, const int* tile_cnt, hipStream_t st) {
   const int items = dm.bh * dm.nb;
-  attn_generic_kernel<T, D><<<items, dm.B, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
-                                                   static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
-                                                   tiles, tile_cnt, tiles == nullptr);
+  // d = 64: 256 threads split each item's key tiles (4 groups at B = 64, 2 at B = 128);
+  // d = 128 keeps one group (two accumulators of 128 floats per thread)
+  if constexpr (D == 64) {
+    if (dm.B == 64)
+      attn_generic_kernel<T, D, 4><<<items, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+                                                          static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
+                                                          tiles, tile_cnt, tiles == nullptr);
+    else
+      attn_generic_kernel<T, D, 2><<<items, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+                                                          static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
+                                                          tiles, tile_cnt, tiles == nullptr);
+  } else {
+    attn_generic_kernel<T, D, 1><<<items, dm.B, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+                                                        static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
+                                                        tiles, tile_cnt, tiles == nullptr);
+  }
 }
 
 }  // namespace
