@@ -93,6 +93,7 @@ class Workload:
     fixed_slash: tuple = ()  # used instead of random draws when given
     fixed_verticals: tuple = ()  # key positions used instead of random draws when given
     batch: int = 1
+    qk_scale: float = 1.0  # power of two multiplying Q and K after rounding (0: all-zero Q and K)
     description: str = ""
 
     @property
@@ -210,6 +211,14 @@ def make_inputs(wl: Workload, with_v: bool = True, q_last_block_only: bool = Fal
     k = np.empty((bkv, n, d), np.float32)
     lib.synth_fill(_ptr(q), bh, n, q0, d, wl.seed, 1, scale, wl.rope_theta, _ptr(q_add), None, None, rb)
     lib.synth_fill(_ptr(k), bkv, n, 0, d, wl.seed, 2, scale, wl.rope_theta, None, _ptr(k_gain), _ptr(k_dir), rb)
+    if wl.qk_scale == 0.0:
+        q[...] = 0.0
+        k[...] = 0.0
+    elif wl.qk_scale != 1.0:
+        m, _ = np.frexp(wl.qk_scale)
+        assert m == 0.5, "qk_scale must be a power of two (exact in both storage types)"
+        q *= np.float32(wl.qk_scale)
+        k *= np.float32(wl.qk_scale)
     if with_v:
         v = np.empty((bkv, n, d), np.float32)
         lib.synth_fill(_ptr(v), bkv, n, 0, d, wl.seed, 3, scale, 0.0, None, None, None, rb)

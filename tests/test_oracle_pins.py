@@ -464,6 +464,20 @@ def test_generator_bf16_storage():
     assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), I.q)
 
 
+def test_generator_qk_scale():
+    """The degenerate-input variants: Q and K scaled exactly (still bf16 values), or zero."""
+    wl = synth.WORKLOADS["llama_32k"].replace(n=600, hq=4, hkv=2, planted_heads=[0])
+    base = synth.make_inputs(wl)
+    big = synth.make_inputs(wl.replace(qk_scale=16.0))
+    zero = synth.make_inputs(wl.replace(qk_scale=0.0))
+    assert np.array_equal(big.q, base.q * 16) and np.array_equal(big.k, base.k * 16)
+    assert np.array_equal(big.v, base.v) and np.array_equal(zero.v, base.v)
+    assert not zero.q.any() and not zero.k.any()
+    assert np.all((big.q.view(np.uint32) & 0xFFFF) == 0)
+    with pytest.raises(AssertionError):
+        synth.make_inputs(wl.replace(qk_scale=3.0))
+
+
 # -------------------------------------------------------- divergence router ----
 def test_log_crisp_within_3ulp_of_log(oracle_lib):
     """Measured bound of the reduction + atanh series: 3 ulp where ln x is small against x
