@@ -14,6 +14,12 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxSeq = 1 << 23;  // keeps every int64 fixed-point row sum below 2^63
+// N_b (N_b + 1) / 2 (PE CSR offsets, flat indices of the pooled map) must fit int32
+constexpr int kMaxBlocks = 65535;
+// (head, query block) items: one-dimensional grids of up to 256-thread
+// workgroups over them stay below 2^32 work-items, and the matrix engine's
+// queue positions fit in 24 bits
+constexpr long long kMaxItems = (1 << 24) - 1;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -61,6 +67,7 @@ crisp_status make_dims(const crisp_shape* sh, const crisp_config* cfg, Dims* dm)
   d.qrows = d.n - d.q0;
   d.dtype = sh->dtype;
   d.ntri = (long long)d.nb * (d.nb + 1) / 2;
+  if (d.nb > kMaxBlocks || (long long)d.bh * d.nb > kMaxItems) return CRISP_ERR_SHAPE;
   *dm = d;
   return CRISP_OK;
 }

@@ -38,6 +38,11 @@
  *   - Supported: head_dim in {64, 128}, block in {64, 128}, n_q_heads a
  *     multiple of n_kv_heads, seq_len >= 1.  The bf16 MFMA attention engine
  *     serves head_dim 128 with block 128; other shapes use a vector-ALU engine.
+ *   - Size limits (CRISP_ERR_SHAPE beyond them): seq_len <= 2^23 (int64
+ *     fixed-point sums), N_b <= 65535 (int32 CSR offsets), batch * n_q_heads
+ *     <= 65535 and batch * n_q_heads * N_b < 2^24 (launch grids over
+ *     (head, query block) items).  Any shape whose workspace fits in one
+ *     GPU's memory is inside them.
  *
  * Numerics of the decision steps (route and index sets) are exactly specified
  * so results are reproducible bit for bit: fp32 proxy scores with a fixed

@@ -55,12 +55,19 @@ def test_sizes(lib):
     assert ws >= 4 * nb * 128 * 128 * 4  # proxy tiles of every head
     assert crisp.workspace_size(_spec(head_dim=96)) == 0
     assert crisp.index_capacity(_spec(n_q_heads=3)) == -1
+    # largest accepted sizes
+    assert crisp.index_capacity(_spec(seq_len=65535 * 128)) == 65535 * 65536 // 2
+    assert crisp.workspace_size(_spec(batch=64, n_q_heads=32, n_kv_heads=8, seq_len=8191 * 128)) > 0
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=96), -2), (dict(n_q_heads=6, n_kv_heads=4), -2), (dict(seq_len=0), -2),
     (dict(seq_len=(1 << 23) + 1), -2), (dict(dtype=7), -3), (dict(block=32), -4), (dict(w_sink=0), -4),
     (dict(tau=(1, 0)), -4), (dict(alpha=(1, 0)), -4), (dict(gamma=(3, 2)), -4), (dict(select_mode=5), -4),
+    # N_b above 65535 (int32 CSR offsets), with either block size
+    (dict(seq_len=65535 * 128 + 1), -2), (dict(seq_len=65535 * 64 + 1, block=64, w_sink=64, w_local=64), -2),
+    # 2^24 (head, query block) items
+    (dict(batch=64, n_q_heads=32, n_kv_heads=8, seq_len=8192 * 128), -2),
 ])
 def test_validation_errors(lib, kw, code):
     s = _spec(**kw)
