@@ -168,7 +168,19 @@ def cpu_baseline(wl, I, seconds_hint=20.0):
                        f"each (marginal cost per row + fixed cost per head); scaled to {wl.hq} heads and "
                        f"{wl.n} rows (extrapolated full-layer time)"),
             "parts_ms": {"route": round(t_route * 1e3, 1), "select": round(t_select * 1e3, 1),
-                         "attention": round(t_att * 1e3, 1)}}
+                         "attention": round(t_att * 1e3, 1)},
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _device_layer(wl):
