@@ -486,6 +486,10 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
           if (a > 0) vload(a - 1);
           if (a < 3) pinf(kf);
           soft_mask(a);
+          // the compiler's small-GEMM interleaving strategy for this region (matrix
+          // instructions spread between the LDS reads and the softmax): 1-2 % faster
+          // than its default schedule on both the sparse and the dense launch
+          __builtin_amdgcn_iglp_opt(0);
           if (a < 3) qk(a + 1);
           if (a < 2) kload(a + 2);
           if (a > 0) { pinf(vf); pv(a - 1); }
