@@ -31,7 +31,7 @@ struct Layout {
   // select
   size_t s_qbar, s_kbar, s_zbar, s_abar, s_rowtot, s_hist, s_state, s_gt, s_tie, s_tiep, s_end;
   // attention
-  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_vt, a_qcnt, a_end;
+  size_t a_tiles, a_cnt, a_ulist, a_ucnt, a_vt, a_part, a_qcnt, a_end;
   // divergence router
   size_t j_qbar, j_kbar, j_zbar, j_abar, j_end;
   size_t total;
@@ -121,6 +121,9 @@ Layout layout(const Dims& d) {
   if (mat) o = align_up(o + pairs * d.nb * sizeof(int));
   L.a_vt = o;
   if (mat) o = align_up(o + (size_t)d.bkv * d.d * d.nb * d.B * 2);  // V^T, bf16
+  L.a_part = o;  // split partials (vector engine)
+  if (!mat && generic_splits(d) > 1)
+    o = align_up(o + (size_t)d.bh * d.nb * generic_splits(d) * d.B * (d.d + 2) * sizeof(float));
   L.a_qcnt = o;
   o = align_up(o + 8 * sizeof(int));  // work-queue counters
   L.a_end = o;
@@ -317,7 +320,8 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
   (void)hipGetLastError();
   if (launch_build_tiles(d, index_out(idx), tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
   if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, w + L.a_vt,
-                       reinterpret_cast<int*>(w + L.a_qcnt), st) != hipSuccess)
+                       reinterpret_cast<int*>(w + L.a_qcnt), reinterpret_cast<float*>(w + L.a_part),
+                       st) != hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }
@@ -339,7 +343,8 @@ crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* c
   char* w = static_cast<char*>(ws);
   (void)hipGetLastError();
   if (launch_attention(d, ba, q, k, v, o, nullptr, nullptr, nullptr, nullptr, w + L.a_vt,
-                       reinterpret_cast<int*>(w + L.a_qcnt), static_cast<hipStream_t>(stream)) != hipSuccess)
+                       reinterpret_cast<int*>(w + L.a_qcnt), reinterpret_cast<float*>(w + L.a_part),
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
     return CRISP_ERR_HIP;
   return hip_status();
 }

@@ -621,22 +621,34 @@ __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, Ind
 
 // ----------------------------------------------------------- vector engine --
 // One thread per query row; keys staged 32 at a time through LDS in fp32.
+//
+// A (head, query block) item is served by S workgroups of G groups of B
+// threads; group g of workgroup s takes the item's tiles t with
+// t mod (S G) = s G + g.  Each thread keeps one query row's running max, sum
+// and output; the groups of a workgroup merge their partial results at the end
+// in group order.  With S = 1 the workgroup writes the output row; otherwise it
+// writes its partial (max, sum, output) to part and attn_generic_merge_kernel
+// combines the S partials in workgroup order.  S > 1 is used when there are
+// too few items to fill the chip (generic_splits).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, T* __restrict__ o,
                                                            Dims dm, BiasArgs bias, const int* __restrict__ tiles,
-                                                           const int* __restrict__ tile_cnt, int dense) {
-  // G groups of B threads split the key tiles of one (head, query block) item
-  // (group g takes tiles g, g + G, ...); each thread keeps one query row's
-  // running max, sum and output, and the groups' partial results are merged
-  // at the end in group order.
+                                                           const int* __restrict__ tile_cnt, int dense, int S,
+                                                           float* __restrict__ part) {
   constexpr int KCH = 32;
-  __shared__ float Kc[G][KCH * D];
-  __shared__ float Vc[G][KCH * D];
+  // key and value chunks of every group; once the key loop is done the merge
+  // buffer for the groups' outputs reuses the same memory (two workgroups fit
+  // one CU's LDS)
+  static_assert(G == 1 || G * KCH >= 64, "merge buffer must fit the chunk buffers");
+  __shared__ float KV[2 * G * KCH * D];
   __shared__ float Cm[G > 1 ? 128 : 1], Cl[G > 1 ? 128 : 1];
-  __shared__ float Ca[G > 1 ? 128 * D : 1];
+  float (*Kc)[KCH * D] = reinterpret_cast<float (*)[KCH * D]>(KV);
+  float (*Vc)[KCH * D] = reinterpret_cast<float (*)[KCH * D]>(KV + G * KCH * D);
+  float* Ca = KV;
+  const int item = blockIdx.x / S, split = blockIdx.x % S;
   int qb, bh;
-  work_item(dm, blockIdx.x, &qb, &bh);
+  work_item(dm, item, &qb, &bh);
   const int B = dm.B;
   const int g = threadIdx.x / B, r = threadIdx.x % B;
   const int i = qb * B + r;
@@ -661,9 +673,11 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
   float m = -__builtin_inff(), l = 0.0f;
   const int ntile = dense ? qb + 1 : tile_cnt[(size_t)bh * dm.nb + qb];
   const int* tl = dense ? nullptr : tiles + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
-  const int rounds = (ntile + G - 1) / G;  // every group runs the same number of rounds (block barriers)
+  // every group of the workgroup runs the same number of rounds (block barriers)
+  const int stride = S * G, first = split * G;
+  const int rounds = ntile > first ? (ntile - first + stride - 1) / stride : 0;
   for (int rd = 0; rd < rounds; ++rd) {
-    const int t = rd * G + g;
+    const int t = rd * stride + first + g;
     const bool active = t < ntile;
     int kb = 0, mode = kModeFull;
     if (active) {
@@ -739,6 +753,17 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
       }
     }
   }
+  if (S > 1) {
+    if (g == 0) {
+      // partial of row r: [max, sum, output[D]]
+      float* pp = part + (((size_t)item * S + split) * B + r) * (D + 2);
+      pp[0] = m;
+      pp[1] = l;
+#pragma unroll
+      for (int t2 = 0; t2 < D; ++t2) pp[2 + t2] = acc[t2];
+    }
+    return;
+  }
   if (g == 0 && i < dm.n) {
     const float inv = 1.0f / l;
     T* op = o + ((size_t)bh * dm.n + i) * D;
@@ -755,31 +780,79 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
   }
 }
 
+// Combines the S partials of each row of an item in workgroup order (the same
+// pairwise rescaling as the in-workgroup merge) and writes the output row.
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_generic_merge_kernel(T* __restrict__ o, Dims dm, int S,
+                                                                 const float* __restrict__ part) {
+  const int item = blockIdx.x, r = threadIdx.x;
+  if (r >= dm.B) return;
+  int qb, bh;
+  work_item(dm, item, &qb, &bh);
+  const int i = qb * dm.B + r;
+  if (i >= dm.n) return;
+  float m = -__builtin_inff(), l = 0.0f, acc[D];
+#pragma unroll
+  for (int t2 = 0; t2 < D; ++t2) acc[t2] = 0.0f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* pp = part + (((size_t)item * S + sp) * dm.B + r) * (D + 2);
+    const float mw = pp[0];
+    const float m_new = mw > m ? mw : m;
+    if (m_new == -__builtin_inff()) continue;
+    const float a0 = expf(m - m_new), a1 = expf(mw - m_new);
+    l = l * a0 + pp[1] * a1;
+#pragma unroll
+    for (int t2 = 0; t2 < D; ++t2) acc[t2] = acc[t2] * a0 + pp[2 + t2] * a1;
+    m = m_new;
+  }
+  const float inv = 1.0f / l;
+  T* op = o + ((size_t)bh * dm.n + i) * D;
+#pragma unroll
+  for (int t2 = 0; t2 < D; ++t2) {
+    const float val = acc[t2] * inv;
+    if constexpr (sizeof(T) == 4) {
+      op[t2] = val;
+    } else {
+      unsigned u = __float_as_uint(val);
+      op[t2] = (bf16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+  }
+}
+
 template <typename T, int D>
 void launch_generic(const Dims& dm, const BiasArgs& bias, const void* q, const void* k, const void* v,
-                    void* o, const int* tiles, const int* tile_cnt, hipStream_t st) {
-  const int items = dm.bh * dm.nb;
+                    void* o, const int* tiles, const int* tile_cnt, float* part, hipStream_t st) {
+  const int S = generic_splits(dm);
+  const int items = dm.bh * dm.nb, grid = items * S;
   // d = 64: 256 threads split each item's key tiles (4 groups at B = 64, 2 at B = 128);
   // d = 128 keeps one group (two accumulators of 128 floats per thread)
   if constexpr (D == 64) {
     if (dm.B == 64)
-      attn_generic_kernel<T, D, 4><<<items, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+      attn_generic_kernel<T, D, 4><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
                                                           static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
-                                                          tiles, tile_cnt, tiles == nullptr);
+                                                          tiles, tile_cnt, tiles == nullptr, S, part);
     else
-      attn_generic_kernel<T, D, 2><<<items, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+      attn_generic_kernel<T, D, 2><<<grid, 256, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
                                                           static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
-                                                          tiles, tile_cnt, tiles == nullptr);
+                                                          tiles, tile_cnt, tiles == nullptr, S, part);
   } else {
-    attn_generic_kernel<T, D, 1><<<items, dm.B, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
+    attn_generic_kernel<T, D, 1><<<grid, dm.B, 0, st>>>(static_cast<const T*>(q), static_cast<const T*>(k),
                                                         static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
-                                                        tiles, tile_cnt, tiles == nullptr);
+                                                        tiles, tile_cnt, tiles == nullptr, S, part);
   }
+  if (S > 1) attn_generic_merge_kernel<T, D><<<items, 128, 0, st>>>(static_cast<T*>(o), dm, S, part);
 }
 
 }  // namespace
 
 bool use_matrix_engine(const Dims& dm) { return dm.dtype == 1 && dm.d == 128 && dm.B == 128; }
+
+int generic_splits(const Dims& dm) {
+  const long long items = (long long)dm.bh * dm.nb;
+  if (items >= kSplitItems) return 1;
+  const long long s = (kSplitItems + items - 1) / items;
+  return (int)(s < kMaxSplits ? s : kMaxSplits);
+}
 
 hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt, int* ulist,
                               int* ucnt, hipStream_t st) {
@@ -798,7 +871,7 @@ __global__ void zero_counters_kernel(int* counters) {
 
 hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q, const void* k,
                             const void* v, void* o, const int* tiles, const int* tile_cnt, const int* ulist,
-                            const int* ucnt, void* vt, int* counters, hipStream_t st) {
+                            const int* ucnt, void* vt, int* counters, float* part, hipStream_t st) {
   if (use_matrix_engine(dm)) {
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
@@ -822,11 +895,11 @@ hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q,
       attn_mfma_kernel<false><<<grid, 512, 0, st>>>(qq, kk, vvt, oo, dm, bias, ulist, ucnt, pairs, npad,
                                                      counters);
   } else if (dm.dtype == 1) {
-    if (dm.d == 128) launch_generic<bf16_t, 128>(dm, bias, q, k, v, o, tiles, tile_cnt, st);
-    else launch_generic<bf16_t, 64>(dm, bias, q, k, v, o, tiles, tile_cnt, st);
+    if (dm.d == 128) launch_generic<bf16_t, 128>(dm, bias, q, k, v, o, tiles, tile_cnt, part, st);
+    else launch_generic<bf16_t, 64>(dm, bias, q, k, v, o, tiles, tile_cnt, part, st);
   } else {
-    if (dm.d == 128) launch_generic<float, 128>(dm, bias, q, k, v, o, tiles, tile_cnt, st);
-    else launch_generic<float, 64>(dm, bias, q, k, v, o, tiles, tile_cnt, st);
+    if (dm.d == 128) launch_generic<float, 128>(dm, bias, q, k, v, o, tiles, tile_cnt, part, st);
+    else launch_generic<float, 64>(dm, bias, q, k, v, o, tiles, tile_cnt, part, st);
   }
   return hipGetLastError();
 }

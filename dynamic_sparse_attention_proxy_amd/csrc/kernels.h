@@ -87,6 +87,13 @@ hipError_t launch_route_jsd(const Dims& dm, unsigned tau_num, unsigned tau_den, 
                             uint8_t* route_jsd, long long* jsd, long long* pooled, hipStream_t st);
 // attention.hip
 bool use_matrix_engine(const Dims& dm);  // bf16, d = 128, B = 128
+// Vector engine: workgroups per (head, query block) item, so that launches with
+// fewer than kSplitItems items still spread over about kSplitItems workgroups
+// (at most kMaxSplits per item).  With S > 1 the partial results take
+// bh * nb * S * B * (d + 2) floats of scratch.
+constexpr long long kSplitItems = 1024;
+constexpr long long kMaxSplits = 8;
+int generic_splits(const Dims& dm);
 // tile lists: for the matrix engine the lists of query-head pairs [bkv * pairs][ntri]
 // + counts [bkv * pairs][nb] (ulist / ucnt), else per-head lists [bh][ntri] + counts
 // [bh][nb] (tiles / tile_cnt)
@@ -94,9 +101,10 @@ hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, in
                               int* ucnt, hipStream_t st);
 // tiles == nullptr: dense causal.  Scratch used by the matrix engine: vt holds V^T of
 // every KV head with keys padded to nb * B (bkv * d * nb * B elements); counters
-// holds the 8 work-queue counters.
+// holds the 8 work-queue counters.  Scratch used by the vector engine: part holds
+// the split partial results (generic_splits).
 hipError_t launch_attention(const Dims& dm, const BiasArgs& bias, const void* q, const void* k,
                             const void* v, void* o, const int* tiles, const int* tile_cnt, const int* ulist,
-                            const int* ucnt, void* vt, int* counters, hipStream_t st);
+                            const int* ucnt, void* vt, int* counters, float* part, hipStream_t st);
 
 }  // namespace crisp
