@@ -629,7 +629,8 @@ __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, Ind
 // in group order.  With S = 1 the workgroup writes the output row; otherwise it
 // writes its partial (max, sum, output) to part and attn_generic_merge_kernel
 // combines the S partials in workgroup order.  S > 1 is used when there are
-// too few items to fill the chip (generic_splits).
+// too few items to fill the chip (generic_splits); workgroup s only exists
+// for an item with more than s G tiles.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, T* __restrict__ o,
@@ -637,6 +638,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
                                                            const int* __restrict__ tile_cnt, int dense, int S,
                                                            float* __restrict__ part) {
   constexpr int KCH = 32;
+  constexpr float kLazy = 16.0f;
   // key and value chunks of every group; once the key loop is done the merge
   // buffer for the groups' outputs reuses the same memory (two workgroups fit
   // one CU's LDS)
@@ -676,6 +678,9 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
   // every group of the workgroup runs the same number of rounds (block barriers)
   const int stride = S * G, first = split * G;
   const int rounds = ntile > first ? (ntile - first + stride - 1) / stride : 0;
+  // a workgroup beyond the item's tiles has nothing to add (the merge skips its
+  // partial) and frees its CU at once, so a launch costs what its tiles cost
+  if (rounds == 0 && S > 1) return;
   for (int rd = 0; rd < rounds; ++rd) {
     const int t = rd * stride + first + g;
     const bool active = t < ntile;
@@ -700,8 +705,9 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
         }
       __syncthreads();
       if (!active) continue;
-      float s[KCH];
-      float cmax = -__builtin_inff();
+      // online softmax with a lazy reference: m moves only when a score exceeds
+      // it by more than kLazy nats, so probabilities stay below e^kLazy and the
+      // output and sum need rescaling only then
       for (int kk = 0; kk < KCH; ++kk) {
         const int cc = sub + kk;
         const int j = kb * B + cc;
@@ -713,22 +719,19 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
         for (int t2 = 0; t2 < 8; ++t2)
           if (boff[t2] == i - j) z += bval[t2];
         const bool ok = j < dm.n && j <= i && tile_keep(mode, diag, r, cc);
-        s[kk] = ok ? z : -__builtin_inff();
-        cmax = s[kk] > cmax ? s[kk] : cmax;
-      }
-      if (cmax == -__builtin_inff()) continue;
-      const float m_new = cmax > m ? cmax : m;
-      const float alpha = expf(m - m_new);
-      l *= alpha;
+        if (!ok) continue;
+        if (z > m + kLazy) {
+          const float alpha = expf(m - z);  // 0 for the first key (m = -inf)
+          l *= alpha;
 #pragma unroll
-      for (int t2 = 0; t2 < D; ++t2) acc[t2] *= alpha;
-      for (int kk = 0; kk < KCH; ++kk) {
-        const float p = expf(s[kk] - m_new);
+          for (int t2 = 0; t2 < D; ++t2) acc[t2] *= alpha;
+          m = z;
+        }
+        const float p = expf(z - m);
         l += p;
 #pragma unroll
         for (int t2 = 0; t2 < D; ++t2) acc[t2] = __builtin_fmaf(p, Vc[g][kk * D + t2], acc[t2]);
       }
-      m = m_new;
     }
   }
   // merge the groups' partial results into group 0, in group order
@@ -783,7 +786,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
 // Combines the S partials of each row of an item in workgroup order (the same
 // pairwise rescaling as the in-workgroup merge) and writes the output row.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void attn_generic_merge_kernel(T* __restrict__ o, Dims dm, int S,
+__global__ __launch_bounds__(128) void attn_generic_merge_kernel(T* __restrict__ o, Dims dm, int S, int G,
+                                                                 const int* __restrict__ tile_cnt, int dense,
                                                                  const float* __restrict__ part) {
   const int item = blockIdx.x, r = threadIdx.x;
   if (r >= dm.B) return;
@@ -791,10 +795,12 @@ __global__ __launch_bounds__(128) void attn_generic_merge_kernel(T* __restrict__
   work_item(dm, item, &qb, &bh);
   const int i = qb * dm.B + r;
   if (i >= dm.n) return;
+  const int ntile = dense ? qb + 1 : tile_cnt[(size_t)bh * dm.nb + qb];
+  const int used = min(S, (ntile + G - 1) / G);  // workgroups that had tiles
   float m = -__builtin_inff(), l = 0.0f, acc[D];
 #pragma unroll
   for (int t2 = 0; t2 < D; ++t2) acc[t2] = 0.0f;
-  for (int sp = 0; sp < S; ++sp) {
+  for (int sp = 0; sp < used; ++sp) {
     const float* pp = part + (((size_t)item * S + sp) * dm.B + r) * (D + 2);
     const float mw = pp[0];
     const float m_new = mw > m ? mw : m;
@@ -840,18 +846,27 @@ void launch_generic(const Dims& dm, const BiasArgs& bias, const void* q, const v
                                                         static_cast<const T*>(v), static_cast<T*>(o), dm, bias,
                                                         tiles, tile_cnt, tiles == nullptr, S, part);
   }
-  if (S > 1) attn_generic_merge_kernel<T, D><<<items, 128, 0, st>>>(static_cast<T*>(o), dm, S, part);
+  if (S > 1)
+    attn_generic_merge_kernel<T, D><<<items, 128, 0, st>>>(static_cast<T*>(o), dm, S, generic_groups(dm), tile_cnt,
+                                                         tiles == nullptr, part);
 }
 
 }  // namespace
 
 bool use_matrix_engine(const Dims& dm) { return dm.dtype == 1 && dm.d == 128 && dm.B == 128; }
 
+int generic_groups(const Dims& dm) { return dm.d == 64 ? (dm.B == 64 ? 4 : 2) : 1; }
+
 int generic_splits(const Dims& dm) {
   const long long items = (long long)dm.bh * dm.nb;
   if (items >= kSplitItems) return 1;
-  const long long s = (kSplitItems + items - 1) / items;
-  return (int)(s < kMaxSplits ? s : kMaxSplits);
+  // about kSplitItems workgroups in all, at most kMaxSplits per item and no
+  // more than the longest item has groups' worth of tiles
+  long long s = (kSplitItems + items - 1) / items;
+  const long long most = (dm.nb + generic_groups(dm) - 1) / generic_groups(dm);
+  if (s > most) s = most;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
 }
 
 hipError_t launch_build_tiles(const Dims& dm, const IndexOut& io, int* tiles, int* tile_cnt, int* ulist,

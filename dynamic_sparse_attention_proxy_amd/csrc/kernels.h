@@ -87,12 +87,14 @@ hipError_t launch_route_jsd(const Dims& dm, unsigned tau_num, unsigned tau_den, 
                             uint8_t* route_jsd, long long* jsd, long long* pooled, hipStream_t st);
 // attention.hip
 bool use_matrix_engine(const Dims& dm);  // bf16, d = 128, B = 128
-// Vector engine: workgroups per (head, query block) item, so that launches with
-// fewer than kSplitItems items still spread over about kSplitItems workgroups
-// (at most kMaxSplits per item).  With S > 1 the partial results take
-// bh * nb * S * B * (d + 2) floats of scratch.
+// Vector engine: groups of B threads per workgroup (generic_groups), and
+// workgroups per (head, query block) item (generic_splits): launches with fewer
+// than kSplitItems items split each item over up to kMaxSplits workgroups.
+// With S > 1 the partial results take bh * nb * S * B * (d + 2) floats of
+// scratch (below kSplitItems * kMaxSplits * B * (d + 2)).
 constexpr long long kSplitItems = 1024;
 constexpr long long kMaxSplits = 8;
+int generic_groups(const Dims& dm);
 int generic_splits(const Dims& dm);
 // tile lists: for the matrix engine the lists of query-head pairs [bkv * pairs][ntri]
 // + counts [bkv * pairs][nb] (ulist / ucnt), else per-head lists [bh][ntri] + counts
