@@ -201,6 +201,8 @@ crisp_status check_list_fields(const crisp_index_sets* idx, const Dims& d) {
   return CRISP_OK;
 }
 
+// Launch failures of one call: every entry point resets the last-error state
+// right before its launches (documented in the header) and reads it after them.
 crisp_status hip_status() {
   return hipGetLastError() == hipSuccess ? CRISP_OK : CRISP_ERR_HIP;
 }

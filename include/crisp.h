@@ -34,7 +34,10 @@
  *     No call synchronises with the host.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     failure a negative crisp_status is returned and nothing is written.
- *     A failed kernel launch returns CRISP_ERR_HIP.
+ *     A failed kernel launch returns CRISP_ERR_HIP.  To tell its own launch
+ *     failures apart, each call resets HIP's last-error state before its
+ *     launches: an error that earlier work of the caller left there is
+ *     dropped, so check it before calling.
  *   - Supported: head_dim in {64, 128}, block in {64, 128}, n_q_heads a
  *     multiple of n_kv_heads, seq_len >= 1.  The bf16 MFMA attention engine
  *     serves head_dim 128 with block 128; other shapes use a vector-ALU engine.
