@@ -168,10 +168,46 @@ class Buffers:
                          self.pe_col.data_ptr(), self.pe_cap)
 
 
-def _bias(offsets, values) -> RelBias:
+def _tensor(t, numel, dtype, what):
+    """Device pointer of t after checking what the C-ABI assumes of it (device memory,
+    contiguous, element type, element count); raises CrispError otherwise."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise CrispError(f"{what}: expected a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise CrispError(f"{what}: expected a contiguous tensor")
+    if t.dtype != dtype:
+        raise CrispError(f"{what}: expected {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise CrispError(f"{what}: expected {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _act_dtype(spec: LayerSpec):
+    import torch
+    return torch.bfloat16 if spec.dtype == BF16 else torch.float32
+
+
+def _qkvo(spec: LayerSpec, **tensors):
+    """Pointers of q / o ([batch, n_q_heads, seq_len, head_dim]) and k / v
+    ([batch, n_kv_heads, seq_len, head_dim]) in the spec's element type."""
+    dt = _act_dtype(spec)
+    per_head = spec.seq_len * spec.head_dim
+    out = {}
+    for name, t in tensors.items():
+        heads = spec.n_q_heads if name in ("q", "o") else spec.n_kv_heads
+        out[name] = _tensor(t, spec.batch * heads * per_head, dt, name)
+    return out
+
+
+def _bias(spec: LayerSpec, offsets, values) -> RelBias:
+    import torch
     if offsets is None or offsets.numel() == 0:
         return RelBias(0, None, None)
-    return RelBias(int(offsets.shape[-1]), offsets.data_ptr(), values.data_ptr())
+    count = int(offsets.shape[-1])
+    n = spec.heads * count
+    return RelBias(count, _tensor(offsets, n, torch.int32, "bias_offsets"),
+                   _tensor(values, n, torch.float32, "bias_values"))
 
 
 def _stream(stream):
@@ -184,39 +220,42 @@ def _stream(stream):
 def route(spec: LayerSpec, q, k, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):
     """crisp_route: proxy map of the last query block, C_struct and route bits into ``bufs``."""
     idx = bufs.index_sets()
-    b = _bias(bias_offsets, bias_values)
-    _check(load_library().crisp_route(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), q.data_ptr(),
-                                      k.data_ptr(), ctypes.byref(b), bufs.ws.data_ptr(), bufs.ws_bytes,
-                                      ctypes.byref(idx), _stream(stream)), "crisp_route")
+    b = _bias(spec, bias_offsets, bias_values)
+    p = _qkvo(spec, q=q, k=k)
+    _check(load_library().crisp_route(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), p["q"], p["k"],
+                                      ctypes.byref(b), bufs.ws.data_ptr(), bufs.ws_bytes, ctypes.byref(idx),
+                                      _stream(stream)), "crisp_route")
 
 
 def select_indices(spec: LayerSpec, q, k, bufs: Buffers, stream=None):
     """crisp_select_indices: VS block lists (Eq. 3-4) and PE block sets (Alg. 4) into ``bufs``."""
     idx = bufs.index_sets()
-    _check(load_library().crisp_select_indices(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
-                                               q.data_ptr(), k.data_ptr(), bufs.ws.data_ptr(), bufs.ws_bytes,
-                                               ctypes.byref(idx), _stream(stream)), "crisp_select_indices")
+    p = _qkvo(spec, q=q, k=k)
+    _check(load_library().crisp_select_indices(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), p["q"],
+                                               p["k"], bufs.ws.data_ptr(), bufs.ws_bytes, ctypes.byref(idx),
+                                               _stream(stream)), "crisp_select_indices")
 
 
 def sparse_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None,
                    stream=None):
     """crisp_sparse_prefill: attention over the selected blocks, written into ``o``."""
     idx = bufs.index_sets()
-    b = _bias(bias_offsets, bias_values)
-    _check(load_library().crisp_sparse_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
-                                               q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(b),
-                                               ctypes.byref(idx), bufs.ws.data_ptr(), bufs.ws_bytes, o.data_ptr(),
-                                               _stream(stream)), "crisp_sparse_prefill")
+    b = _bias(spec, bias_offsets, bias_values)
+    p = _qkvo(spec, q=q, k=k, v=v, o=o)
+    _check(load_library().crisp_sparse_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), p["q"],
+                                               p["k"], p["v"], ctypes.byref(b), ctypes.byref(idx),
+                                               bufs.ws.data_ptr(), bufs.ws_bytes, p["o"], _stream(stream)),
+           "crisp_sparse_prefill")
 
 
 def dense_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None,
                   stream=None):
     """crisp_dense_prefill: full causal attention with the same tile engine (``bufs`` supplies the workspace)."""
-    b = _bias(bias_offsets, bias_values)
-    _check(load_library().crisp_dense_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
-                                              q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(b),
-                                              bufs.ws.data_ptr(), bufs.ws_bytes, o.data_ptr(), _stream(stream)),
-           "crisp_dense_prefill")
+    b = _bias(spec, bias_offsets, bias_values)
+    p = _qkvo(spec, q=q, k=k, v=v, o=o)
+    _check(load_library().crisp_dense_prefill(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), p["q"],
+                                              p["k"], p["v"], ctypes.byref(b), bufs.ws.data_ptr(), bufs.ws_bytes,
+                                              p["o"], _stream(stream)), "crisp_dense_prefill")
 
 
 def route_jsd(spec: LayerSpec, q, k, bufs: Buffers, route_out, jsd_out, tau_jsd=(1, 100), pooled_out=None,
@@ -224,12 +263,16 @@ def route_jsd(spec: LayerSpec, q, k, bufs: Buffers, route_out, jsd_out, tau_jsd=
     """crisp_route_jsd: the divergence router on the proxy that ``route`` left in ``bufs``.
     route_out [BH] uint8, jsd_out [BH] int64 (JSD = value * 2^-53), pooled_out [BH, N_b]
     int64 or None."""
+    import torch
     idx = bufs.index_sets()
+    p = _qkvo(spec, q=q, k=k)
+    bh = spec.heads
+    r_ptr = _tensor(route_out, bh, torch.uint8, "route_out")
+    j_ptr = _tensor(jsd_out, bh, torch.int64, "jsd_out")
+    p_ptr = None if pooled_out is None else _tensor(pooled_out, bh * spec.num_blocks, torch.int64, "pooled_out")
     _check(load_library().crisp_route_jsd(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), tau_jsd[0],
-                                          tau_jsd[1], q.data_ptr(), k.data_ptr(), ctypes.byref(idx),
-                                          bufs.ws.data_ptr(), bufs.ws_bytes, route_out.data_ptr(), jsd_out.data_ptr(),
-                                          None if pooled_out is None else pooled_out.data_ptr(), _stream(stream)),
-           "crisp_route_jsd")
+                                          tau_jsd[1], p["q"], p["k"], ctypes.byref(idx), bufs.ws.data_ptr(),
+                                          bufs.ws_bytes, r_ptr, j_ptr, p_ptr, _stream(stream)), "crisp_route_jsd")
 
 
 def prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):

@@ -148,3 +148,13 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text and "liboracle" not in text, f
+
+
+def test_binding_rejects_host_tensors():
+    """The binding hands the C-ABI device pointers only: host tensors are refused
+    before any call is made."""
+    import torch
+    with pytest.raises(crisp.CrispError, match="CUDA"):
+        crisp._tensor(torch.zeros(4), 4, torch.float32, "q")
+    with pytest.raises(crisp.CrispError, match="CUDA"):
+        crisp._qkvo(_spec(), q=torch.zeros(4 * 1000 * 128, dtype=torch.bfloat16))

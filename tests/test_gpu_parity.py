@@ -247,6 +247,27 @@ def test_gamma_variant(mode):
             checked += 1
 
 
+@pytest.mark.timeout(120)
+def test_binding_checks_tensors():
+    """Wrong element type, layout or size is refused before anything is launched."""
+    import torch
+    wl = EDGE["ragged_bf16"]
+    spec = spec_for(wl)
+    bufs = crisp.Buffers(spec)
+    q = torch.zeros(wl.hq, wl.n, wl.d, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(wl.hkv, wl.n, wl.d, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(crisp.CrispError, match="expected torch.bfloat16"):
+        crisp.route(spec, q.float(), k, bufs)
+    with pytest.raises(crisp.CrispError, match="contiguous"):
+        crisp.route(spec, q.transpose(1, 2), k, bufs)
+    with pytest.raises(crisp.CrispError, match="elements"):
+        crisp.select_indices(spec, q.reshape(-1)[:-8], k, bufs)
+    with pytest.raises(crisp.CrispError, match="bias_offsets"):
+        crisp.route(spec, q, k, bufs, torch.zeros(wl.hq, 2, dtype=torch.int64, device="cuda"),
+                    torch.zeros(wl.hq, 2, device="cuda"))
+    torch.cuda.synchronize()
+
+
 @pytest.mark.timeout(600)
 def test_determinism():
     wl, I, X, spec, bufs, ref = _case("llama_32k")
