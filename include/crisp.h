@@ -27,8 +27,10 @@
  *     ceil(seq_len / block).  The proxy query subset is the last query block,
  *     rows (N_b - 1) * block .. seq_len - 1 (qrows rows).
  *   - The library never allocates or frees device memory and keeps no state:
- *     `ws` is scratch for the duration of one call (its contents are not kept
- *     between calls).  Pointers must be 16-byte aligned.
+ *     `ws` is scratch for the duration of one call (no call reads what an
+ *     earlier call left in it; results pass between calls in idx).  Calls that
+ *     can run at the same time (on different streams) need separate
+ *     workspaces.  Pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     kernels and return; results are valid once the stream has completed.
  *     No call synchronises with the host.
