@@ -120,6 +120,10 @@ WORKLOADS = {
         name="llama_32k", hq=32, hkv=8, d=128, n=32768, dtype="bf16", block=128, rope_theta=5e5,
         seed=1002, planted_heads=list(range(16)),
         description="Llama-3.1-8B-shaped layer: 32 q / 8 kv heads, d=128, n=32768, bf16, causal"),
+    "llama_64k": Workload(
+        name="llama_64k", hq=32, hkv=8, d=128, n=65536, dtype="bf16", block=128, rope_theta=5e5,
+        seed=1006, planted_heads=list(range(16)),
+        description="Llama-3.1-8B-shaped layer: 32 q / 8 kv heads, d=128, n=65536, bf16, causal"),
     "llama_128k": Workload(
         name="llama_128k", hq=32, hkv=8, d=128, n=131072, dtype="bf16", block=128, rope_theta=5e5,
         seed=1003, planted_heads=list(range(16)),
@@ -128,6 +132,10 @@ WORKLOADS = {
         name="qwen_128k", hq=28, hkv=4, d=128, n=131072, dtype="bf16", block=128, rope_theta=1e6,
         seed=1004, planted_heads=list(range(14)), sink_gain=8.0,
         description="Qwen2.5-7B-shaped layer: 28 q / 4 kv heads, d=128, n=131072, bf16, causal"),
+    "llama_256k": Workload(
+        name="llama_256k", hq=32, hkv=8, d=128, n=262144, dtype="bf16", block=128, rope_theta=5e5,
+        seed=1007, planted_heads=list(range(16)),
+        description="Llama-3.1-8B-shaped layer: 32 q / 8 kv heads, d=128, n=262144, bf16, causal"),
     "llama_512k": Workload(
         name="llama_512k", hq=32, hkv=8, d=128, n=524288, dtype="bf16", block=128, rope_theta=5e5,
         seed=1005, planted_heads=list(range(16)), n_vertical=256, n_slash=8,
