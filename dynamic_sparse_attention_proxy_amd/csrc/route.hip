@@ -172,6 +172,8 @@ __global__ __launch_bounds__(kThreads) void proxy_scores_kernel(const T* __restr
 // Thread layout of the streaming passes over one (head, key block) tile stored
 // [key c][row r]: each thread owns 4 consecutive rows and visits keys
 // c = cp, cp + CP, ... ; float4 loads are contiguous across the row groups.
+constexpr int kRowsumTiles = 4;  // key blocks per workgroup of proxy_rowsum_kernel
+
 template <int B>
 struct StreamLayout {
   static constexpr int RG = B / 4;
@@ -185,43 +187,45 @@ __global__ __launch_bounds__(kThreads) void proxy_rowsum_kernel(Dims dm, const f
                                                                 long long* __restrict__ L) {
   using Lay = StreamLayout<B>;
   __shared__ long long red[Lay::CP][B];
-  const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int bh = blockIdx.y, tid = threadIdx.x;
   const int rg = tid % Lay::RG, cp = tid / Lay::RG;
-  const long long tile_off = ((long long)bh * dm.nb + kb) * (long long)(B * B);
   float m[4];
   long long acc[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < 4; ++e) m[e] = ordered_to_float(m_enc[bh * B + rg * 4 + e]);
-  if (kb < dm.nb - 1 && dm.qrows == B) {
-    // every (row, key) of the tile is valid: integer-valued terms summed in fp64
-    // (at most IT terms of <= 2^40 each, exact)
-    double accd[4] = {0.0, 0.0, 0.0, 0.0};
+  // kRowsumTiles consecutive key blocks per workgroup; full tiles accumulate
+  // integer-valued terms in fp64 (at most kRowsumTiles * IT terms of <= 2^40
+  // each, exact)
+  double accd[4] = {0.0, 0.0, 0.0, 0.0};
+  const int kb0 = blockIdx.x * kRowsumTiles, kb1 = min(kb0 + kRowsumTiles, dm.nb);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const long long tile_off = ((long long)bh * dm.nb + kb) * (long long)(B * B);
+    if (kb < dm.nb - 1 && dm.qrows == B) {
 #pragma unroll 4
-    for (int it = 0; it < Lay::IT; ++it) {
-      const int c = cp + Lay::CP * it;
-      const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
-      const float z[4] = {z4.x, z4.y, z4.z, z4.w};
+      for (int it = 0; it < Lay::IT; ++it) {
+        const int c = cp + Lay::CP * it;
+        const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
+        const float z[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accd[e] += (double)fix_rne_f(exp_crisp(z[e] - m[e]));
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = (long long)accd[e];
-  } else {
+        for (int e = 0; e < 4; ++e) accd[e] += (double)fix_rne_f(exp_crisp(z[e] - m[e]));
+      }
+    } else {
 #pragma unroll 4
-    for (int it = 0; it < Lay::IT; ++it) {
-      const int c = cp + Lay::CP * it;
-      const int jj = kb * B + c;
-      const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
-      const float z[4] = {z4.x, z4.y, z4.z, z4.w};
+      for (int it = 0; it < Lay::IT; ++it) {
+        const int c = cp + Lay::CP * it;
+        const int jj = kb * B + c;
+        const float4 z4 = *reinterpret_cast<const float4*>(S + tile_off + (size_t)c * B + rg * 4);
+        const float z[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rg * 4 + e;
-        if (r < dm.qrows && jj <= dm.q0 + r) acc[e] += fix_rne(exp_crisp(z[e] - m[e]));
+        for (int e = 0; e < 4; ++e) {
+          const int r = rg * 4 + e;
+          if (r < dm.qrows && jj <= dm.q0 + r) acc[e] += fix_rne(exp_crisp(z[e] - m[e]));
+        }
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) red[cp][rg * 4 + e] = acc[e];
+  for (int e = 0; e < 4; ++e) red[cp][rg * 4 + e] = acc[e] + (long long)accd[e];
   __syncthreads();
   if (tid < B && tid < dm.qrows) {
     long long s = 0;
@@ -373,10 +377,12 @@ hipError_t launch_route(const Dims& dm, const RouteArgs& ra, const BiasArgs& bia
   }
 #undef CRISP_SCORES
   if (dm.B == 128) {
-    proxy_rowsum_kernel<128><<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, ws.S, ws.m_enc, ws.L);
+    proxy_rowsum_kernel<128><<<dim3((dm.nb + kRowsumTiles - 1) / kRowsumTiles, dm.bh), kThreads, 0, st>>>(
+        dm, ws.S, ws.m_enc, ws.L);
     proxy_mass_kernel<128><<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, ra, ws.S, ws.m_enc, ws.L, ws.part);
   } else {
-    proxy_rowsum_kernel<64><<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, ws.S, ws.m_enc, ws.L);
+    proxy_rowsum_kernel<64><<<dim3((dm.nb + kRowsumTiles - 1) / kRowsumTiles, dm.bh), kThreads, 0, st>>>(
+        dm, ws.S, ws.m_enc, ws.L);
     proxy_mass_kernel<64><<<dim3(dm.nb, dm.bh), kThreads, 0, st>>>(dm, ra, ws.S, ws.m_enc, ws.L, ws.part);
   }
   route_finish_kernel<<<dm.bh, kThreads, 0, st>>>(dm, ra, ws.part, io);
