@@ -269,6 +269,44 @@ def test_binding_checks_tensors():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny", "llama_32k"])
+def test_graph_replay_matches_eager(name):
+    """The whole layer (route, select, sparse attention) captured in a HIP graph: the
+    library allocates, clears with memset and synchronises nothing, so every replay,
+    with eager work of the program in between, gives the eager bits."""
+    import torch
+    wl, I, X, spec, bufs, ref = _case(name)
+    o_eager = torch.empty_like(X.q)
+    crisp.prefill(spec, X.q, X.k, X.v, o_eager, bufs, X.bias_offsets, X.bias_values)
+    torch.cuda.synchronize()
+    gb = crisp.Buffers(spec)
+    o = torch.empty_like(X.q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager call on the capture stream first
+        crisp.prefill(spec, X.q, X.k, X.v, o, gb, X.bias_offsets, X.bias_values)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        crisp.prefill(spec, X.q, X.k, X.v, o, gb, X.bias_offsets, X.bias_values)
+    torch.cuda.synchronize()
+    od = torch.empty_like(X.q)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        gb.route.fill_(7)
+        gb.pe_rowptr.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager), f"replay {rep}: output"
+        bad = compare_index_sets(download_index_sets(gb), ref)
+        assert not bad, f"replay {rep}: " + "\n".join(bad[:5])
+        crisp.dense_prefill(spec, X.q, X.k, X.v, od, gb, X.bias_offsets, X.bias_values)  # eager work between
+        torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(600)
 def test_determinism():
     wl, I, X, spec, bufs, ref = _case("llama_32k")
     import torch
