@@ -234,15 +234,6 @@ __global__ __launch_bounds__(kThreads) void proxy_rowsum_kernel(Dims dm, const f
   }
 }
 
-// fl32(e / l) for 0 <= e <= 1 <= l (fp32), from rl = fl64(1 / l): the fp64
-// product e rl is within 2^-52 (relative) of e / l, while a quotient of two
-// fp32 numbers that is a normal fp32 number lies at least 2^-49 (relative) from
-// every rounding midpoint of fp32 (it is never one), so rounding the product
-// to fp32 gives the correctly rounded quotient.  Below 2^-126 the two may
-// differ, but every such value is below 2^-41, where the fixed-point
-// conversion that follows gives 0 either way.
-__device__ __forceinline__ float div_by_l(float e, double rl) { return (float)((double)e * rl); }
-
 template <int B>
 __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs ra,
                                                               const float* __restrict__ S,
@@ -254,12 +245,11 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
   const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int rg = tid % Lay::RG, cp = tid / Lay::RG;
   const long long tile_off = ((long long)bh * dm.nb + kb) * (long long)(B * B);
-  float m[4];
-  double rl[4];  // 1 / l in fp64: quotients by l without a division per element
+  float m[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     m[e] = ordered_to_float(m_enc[bh * B + rg * 4 + e]);
-    rl[e] = 1.0 / (double)fix_to_float(L[bh * B + rg * 4 + e]);
+    l[e] = fix_to_float(L[bh * B + rg * 4 + e]);
   }
   long long lo = 0, up = 0, an = 0;
   const bool plain = kb < dm.nb - 1 && dm.qrows == B && kb * B >= ra.w_sink &&
@@ -275,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
       const float z[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double aq = (double)fix_rne_f(div_by_l(exp_crisp(z[e] - m[e]), rl[e]));
+        const double aq = (double)fix_rne_f(exp_crisp(z[e] - m[e]) / l[e]);
         alld += aq;
         lod += rg * 4 + e >= c ? aq : 0.0;
       }
@@ -295,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
       const int ii = dm.q0 + r;
       if (r < dm.qrows && jj <= ii) {
         const float ev = exp_crisp(z[e] - m[e]);
-        const long long aq = fix_rne(div_by_l(ev, rl[e]));
+        const long long aq = fix_rne(ev / l[e]);
         // slash block (i - j) / B is (nb - 1 - kb) when r >= c, one less when r < c
         if (r >= c)
           lo += aq;

@@ -596,26 +596,3 @@ def test_jsd_route_matches_fp64_writing_and_separates_heads(oracle_lib):
     assert out["route"].tolist() == [1 if h in wl.planted_heads else 0 for h in range(wl.hq)]
     assert out["route"].tolist() == pr["route"].tolist()
 
-
-def test_quotient_by_fp64_reciprocal_rounds_like_division():
-    """The identity the GPU's block-mass pass relies on instead of an fp32 division
-    per element: for fp32 0 <= e <= 1 <= l, fl32(fl64(e * fl64(1/l))) equals the
-    correctly rounded fl32(e / l) whenever the quotient is a normal fp32 number, and
-    below that both give rne(q * 2^40) = 0."""
-    rng = np.random.default_rng(91)
-    N = 2_000_000
-    e = np.concatenate([rng.random(N // 2), np.exp(rng.uniform(-80.0, 0.0, N // 2))]).astype(np.float32)
-    l = np.concatenate([rng.uniform(1.0, 2.0, N // 2), np.exp(rng.uniform(0.0, 15.9, N // 2))]).astype(np.float32)
-    # quotients near rounding midpoints: e chosen as (odd multiple of a half ulp of q) * l, rounded to fp32
-    q0 = rng.uniform(0.5, 1.0, N // 4).astype(np.float32)
-    l2 = rng.uniform(1.0, 2.0, N // 4).astype(np.float32)
-    mid = q0.astype(np.float64) + np.spacing(q0).astype(np.float64) / 2
-    e2 = np.minimum(mid * l2, 1.0).astype(np.float32)
-    e = np.concatenate([e, e2, np.zeros(1, np.float32), np.ones(1, np.float32)])
-    l = np.concatenate([l, l2, np.ones(1, np.float32), np.ones(1, np.float32)])
-    exact = (e / l).astype(np.float32)  # numpy float32 division: IEEE round-to-nearest
-    via64 = (e.astype(np.float64) * (1.0 / l.astype(np.float64))).astype(np.float32)
-    normal = exact >= np.float32(2.0 ** -126)
-    assert np.array_equal(exact[normal], via64[normal])
-    fix = lambda v: np.rint(np.ldexp(v.astype(np.float64), 40)).astype(np.int64)
-    assert np.array_equal(fix(exact), fix(via64))
