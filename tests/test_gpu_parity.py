@@ -341,6 +341,12 @@ EDGE = {
                                   rope_theta=5e5, seed=37, planted_heads=[0, 1], n_vertical=5, batch=2),
     "f32_b128_d128": synth.Workload(name="f32_b128_d128", hq=2, hkv=1, d=128, n=1500, dtype="f32", block=128,
                                     rope_theta=0.0, seed=38, planted_heads=[0], n_vertical=3),
+    # GQA groups of 8 (four full head pairs per KV head) and of 3 (the second pair
+    # of each KV head has one head) on the matrix engine
+    "gqa8_bf16": synth.Workload(name="gqa8", hq=8, hkv=1, d=128, n=6000, dtype="bf16", block=128,
+                                rope_theta=5e5, seed=44, planted_heads=[0, 3, 4], n_vertical=5),
+    "gqa3_bf16": synth.Workload(name="gqa3", hq=6, hkv=2, d=128, n=5200, dtype="bf16", block=128,
+                                rope_theta=5e5, seed=45, planted_heads=[2, 3], n_vertical=4),
     # Degenerate inputs.  Q = K = 0: every causal key of a row ties, so all full key
     # blocks carry the same vertical mass (the noise floor keeps only the first and
     # last block), every pooled row is uniform (the PE selection is decided by ties),
