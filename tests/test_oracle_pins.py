@@ -146,7 +146,7 @@ def test_proxy_pooling_recount(oracle_lib):
         assert pr["mass_v"][h].sum() == pr["mass_s"][h].sum() == pr["total"][h]
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama_32k", "llama_64k", "llama_128k", "qwen_128k", "llama_256k"])
+@pytest.mark.parametrize("name", ["tiny", "llama_32k", "llama_64k", "llama_128k", "qwen_128k", "llama_256k", "llama_512k"])
 def test_routing_planted_vs_high_entropy(oracle_lib, name):
     """Low-entropy (planted) heads route to VS, i.i.d. heads to pooled estimation (Eq. 2 + routing rule)."""
     wl = synth.WORKLOADS[name]
