@@ -141,7 +141,9 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // lds_wave + kBufImm addresses the slot: lds_wave is a per-wave scalar, the
-// constant part is encoded in the instruction stream.
+// constant part is encoded in the instruction stream.  The LDS destination goes
+// through m0; nothing else in these kernels uses m0 (checked in the generated
+// code), so the compiler's treatment of m0 as reserved does not matter here.
 template <unsigned kLdsConst>
 __device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, unsigned lds_wave) {
   asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"

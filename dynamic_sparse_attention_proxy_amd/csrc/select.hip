@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void pe_radix_hist_kernel(Dims dm, IndexO
 // Find the digit where the running mass (from the largest values down) first
 // reaches the remaining target R; everything in higher buckets is inside the
 // prefix.  After the last pass the full cut value v* is known.
-__global__ __launch_bounds__(kThreads) void pe_radix_scan_kernel(Dims dm, IndexOut io, int pass,
+__global__ __launch_bounds__(kThreads) void pe_radix_scan_kernel(IndexOut io, int pass,
                                                                  const unsigned long long* __restrict__ hist,
                                                                  long long* __restrict__ state) {
   __shared__ long long part[kThreads];
@@ -611,7 +611,7 @@ hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, co
     for (int pass = 0; pass < 4; ++pass) {
       pe_radix_hist_kernel<<<dim3(nchunks, dm.bh), kThreads, 0, st>>>(dm, io, pass, ws.abar, ws.hist,
                                                                         ws.state, chunk);
-      pe_radix_scan_kernel<<<dm.bh, kThreads, 0, st>>>(dm, io, pass, ws.hist, ws.state);
+      pe_radix_scan_kernel<<<dm.bh, kThreads, 0, st>>>(io, pass, ws.hist, ws.state);
     }
     pe_count_kernel<<<rows, kThreads, 0, st>>>(dm, io, ws.abar, ws.state, ws.gtcnt, ws.tiecnt);
   }
