@@ -8,6 +8,8 @@ import numpy as np
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import bench  # noqa: E402
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 
 class _T:
     def __init__(self, a):
@@ -71,3 +73,14 @@ def test_tile_counts_bruteforce():
                         if qb * B + r >= kb * B + c)
                     for qb in range(nb) for kb in range(qb + 1))
         assert got[h] == tiles, (h, got[h], tiles)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path runs on one GPU; asking for more exits with a message, before any GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "--gpus 1" in r.stderr
+    assert not r.stdout.strip()
