@@ -140,6 +140,10 @@ WORKLOADS = {
         name="llama_512k", hq=32, hkv=8, d=128, n=524288, dtype="bf16", block=128, rope_theta=5e5,
         seed=1005, planted_heads=list(range(16)), n_vertical=256, n_slash=8,
         description="Llama-3.1-8B-shaped layer: 32 q / 8 kv heads, d=128, n=524288, bf16, causal"),
+    "llama_1m": Workload(
+        name="llama_1m", hq=32, hkv=8, d=128, n=1 << 20, dtype="bf16", block=128, rope_theta=5e5,
+        seed=1008, planted_heads=list(range(16)), n_vertical=256, n_slash=8,
+        description="Llama-3.1-8B-shaped layer: 32 q / 8 kv heads, d=128, n=1048576, bf16, causal"),
 }
 
 

@@ -6,6 +6,7 @@ against the fp64 oracle on the same index sets.  Below 128K every row is
 checked; at 128K and above the full index sets plus 256 seeded rows per head.
 """
 import gc
+import os
 
 import numpy as np
 import pytest
@@ -384,3 +385,39 @@ def test_edge_shapes(name, mode):
     if mode == crisp.SELECT_KEEP_ALL:
         import torch
         assert torch.equal(run_sparse(spec, X, bufs), run_dense(spec, X))
+
+
+@pytest.mark.timeout(1200)
+def test_long_context_1m():
+    """Beyond the longest workload: a 1M-token layer through the whole path.  The GPU
+    routes and selects every head; the oracle recomputes one planted and one i.i.d.
+    head (routing outputs and index sets bit-exact) and 256 sampled rows of both."""
+    import torch
+    _cache.clear()
+    gc.collect()
+    wl = synth.WORKLOADS["llama_1m"]
+    with Timer("inputs 1m"):
+        I = synth.make_inputs(wl)
+    X = DeviceInputs(I)
+    spec = spec_for(wl)
+    with Timer("gpu route+select 1m"):
+        bufs = run_route_select(spec, X)
+    gpu = download_index_sets(bufs)
+    assert gpu["route"].tolist() == [1 if h in wl.planted_heads else 0 for h in range(wl.hq)]
+    heads, kvs = [0, 16], [0, 16 // (wl.hq // wl.hkv)]
+    with Timer("oracle index sets 1m (2 heads)"):
+        ref = oracle.index_sets(I.q[heads], I.k[kvs], wl.block, wl.w_sink, wl.w_local, synth.TAU, synth.ALPHA,
+                                synth.GAMMA, I.bias_offsets[heads], I.bias_values[heads])
+    sub = {key: gpu[key][heads] for key in ("route", "cnum", "mass_v", "mass_s", "total")}
+    sub["heads"] = [gpu["heads"][h] for h in heads]
+    bad = compare_index_sets(sub, ref)
+    assert not bad, "\n".join(bad[:20])
+    rows = synth.sample_rows(wl)
+    with Timer("gpu sparse 1m"):
+        o = rows_of(run_sparse(spec, X, bufs)[torch.as_tensor(heads, device="cuda")], rows)
+    with Timer("oracle attention 1m (2 heads, 256 rows)"):
+        r = oracle.attention(I.q[heads], I.k[kvs], I.v[kvs], wl.block, oracle.specs_from_index_sets(ref), rows=rows,
+                             bias_offsets=I.bias_offsets[heads], bias_values=I.bias_values[heads], chunk=512)
+    err = np.abs(o - r).max()
+    log("1m max-abs", err)
+    assert np.isfinite(o).all() and err <= TOL["bf16"]
