@@ -241,7 +241,8 @@ def _variant_stats(wl, X, **overrides):
     return row
 
 
-def selection_sweep(names=("llama_32k", "llama_64k", "llama_128k", "llama_256k", "qwen_128k", "llama_512k")):
+def selection_sweep(names=("llama_32k", "llama_64k", "llama_128k", "llama_256k", "qwen_128k", "llama_512k",
+                           "llama_1m")):
     """Selected budget and sparse-attention time of the noise-floor rule against the
     cumulative-coverage rule, over sequence length (VS heads; PE heads are the same)."""
     import torch
