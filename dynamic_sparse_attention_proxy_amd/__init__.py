@@ -62,6 +62,10 @@ def load_library(path: str = None):
     global _lib
     path = path or os.environ.get("CRISP_LIB") or LIB_PATH
     if _lib is None:
+        # torch first, so that the library binds to the HIP runtime torch brings
+        # rather than pulling in the system's ahead of it (the two do not mix in
+        # one process: kernel launches then fail)
+        import torch  # noqa: F401
         if not os.path.exists(path):
             raise CrispError(f"{path} is missing: build it with `python -m dynamic_sparse_attention_proxy_amd.build`")
         lib = ctypes.CDLL(path)
