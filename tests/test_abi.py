@@ -158,3 +158,14 @@ def test_binding_rejects_host_tensors():
         crisp._tensor(torch.zeros(4), 4, torch.float32, "q")
     with pytest.raises(crisp.CrispError, match="CUDA"):
         crisp._qkvo(_spec(), q=torch.zeros(4 * 1000 * 128, dtype=torch.bfloat16))
+
+
+def test_library_loads_after_torch():
+    """libcrisp.so must bind to the HIP runtime torch brings: loading it imports torch
+    first, even in a process that has not imported torch yet."""
+    import subprocess
+    import sys
+    code = ("import sys; import dynamic_sparse_attention_proxy_amd as c; assert 'torch' not in sys.modules; "
+            "c.load_library(); assert 'torch' in sys.modules; print('ok')")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
