@@ -26,7 +26,8 @@
  *   - every sum that feeds a decision is an int64 fixed-point sum of
  *     rne(value * 2^40), so its value does not depend on summation order;
  *   - thresholds are compared as exact integers.
- * Build: gcc -O2 -ffp-contract=off (no contraction, no fast-math).
+ * Build: gcc -O2 -ffp-contract=off -mfma -fopenmp (no contraction, no
+ * fast-math; -mfma makes fmaf a single fused instruction rather than a call).
  */
 #include <math.h>
 #include <omp.h>
