@@ -161,6 +161,26 @@ def cpu_baseline(wl, I, seconds_hint=20.0):
         per_head.append(fixed + marginal * wl.n)
     t_att = per_head[0] * n_vs + per_head[1] * (wl.hq - n_vs)
     total_ms = (t_route + t_select + t_att) * 1e3
+    # the same attention sample on one thread (attention is all but 0.2 % of the
+    # oracle's time at this size)
+    nt = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        per_head_1 = []
+        for h in heads:
+            times = []
+            for nrows in (8, 24):
+                rows = np.sort(rng.choice(wl.n, size=nrows, replace=False))
+                t = time.perf_counter()
+                oracle.attention(I.q, I.k, I.v, wl.block, specs, rows=rows, bias_offsets=I.bias_offsets,
+                                 bias_values=I.bias_values, heads=[h], chunk=64)
+                times.append(time.perf_counter() - t)
+            marginal = max(times[1] - times[0], 0.0) / 16
+            fixed = max(times[0] - 8 * marginal, 0.0)
+            per_head_1.append(fixed + marginal * wl.n)
+    finally:
+        torch.set_num_threads(nt)
+    t_att_1 = per_head_1[0] * n_vs + per_head_1[1] * (wl.hq - n_vs)
     return {"value": round(total_ms, 1), "unit": "ms/layer", "cores": max(threads, torch.get_num_threads()),
             "kind": "oracle",
             "sample": (f"oracle timed on heads {heads} (one VS, one PE): full proxy routing of both, VS selection, "
@@ -169,7 +189,11 @@ def cpu_baseline(wl, I, seconds_hint=20.0):
                        f"{wl.n} rows (extrapolated full-layer time)"),
             "parts_ms": {"route": round(t_route * 1e3, 1), "select": round(t_select * 1e3, 1),
                          "attention": round(t_att * 1e3, 1)},
-            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread_attention": {
+                "value": round(t_att_1 * 1e3, 1), "unit": "ms/layer", "cores": 1,
+                "sample": "the oracle's fp64 attention alone on one thread: 8 and 24 uniform rows of the same "
+                          "two heads, scaled like the attention part above"}}
 
 
 def _cpu_model() -> str:
