@@ -308,6 +308,30 @@ def test_graph_replay_matches_eager(name):
 
 
 @pytest.mark.timeout(600)
+def test_two_streams_with_own_workspaces():
+    """The library keeps no state: two layers in flight on two streams, each with its
+    own workspace and index buffers, give the bits of the same calls run alone."""
+    import torch
+    wl, I, X, spec, bufs, ref = _case("llama_32k")
+    o_ref = torch.empty_like(X.q)
+    crisp.prefill(spec, X.q, X.k, X.v, o_ref, bufs, X.bias_offsets, X.bias_values)
+    torch.cuda.synchronize()
+    b1, b2 = crisp.Buffers(spec), crisp.Buffers(spec)
+    o1, o2 = torch.empty_like(X.q), torch.empty_like(X.q)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(2):
+        crisp.prefill(spec, X.q, X.k, X.v, o1, b1, X.bias_offsets, X.bias_values, stream=s1)
+        crisp.prefill(spec, X.q, X.k, X.v, o2, b2, X.bias_offsets, X.bias_values, stream=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o_ref) and torch.equal(o2, o_ref)
+    for b in (b1, b2):
+        bad = compare_index_sets(download_index_sets(b), ref)
+        assert not bad, "\n".join(bad[:5])
+
+
+@pytest.mark.timeout(600)
 def test_determinism():
     wl, I, X, spec, bufs, ref = _case("llama_32k")
     import torch
