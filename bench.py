@@ -350,7 +350,6 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
 
     import dynamic_sparse_attention_proxy_amd as crisp
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     t = time.time()
     I = synth.make_inputs(wl)
     log(f"inputs {wl.name}: {time.time() - t:.1f}s")

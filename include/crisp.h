@@ -175,8 +175,13 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
                                   const crisp_index_sets* idx, void* ws, size_t ws_bytes, void* o,
                                   void* stream);
 
-/* Full causal attention (the dense baseline; same tile engine).  Reads q, k,
- * v, bias; uses ws as scratch; writes o. */
+/* Full causal attention: the dense baseline the sparse path is measured
+ * against.  On the CRISP summary page the comparator is exact full attention
+ * computed with FlashAttention (Results: the legend of Table 2, and the
+ * attention-only latencies of Latency Scaling, Table 4, quoted as speedups
+ * over it).  Here it is the same tile engine as crisp_sparse_prefill with every
+ * causal key tile listed, so the two differ only in the tiles they visit.
+ * Reads q, k, v, bias; uses ws as scratch; writes o. */
 crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
                                  const void* k, const void* v, const crisp_rel_bias* bias, void* ws,
                                  size_t ws_bytes, void* o, void* stream);

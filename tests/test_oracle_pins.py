@@ -90,6 +90,13 @@ def test_proxy_closed_form_zero_queries(oracle_lib, n, B, w):
         assert pr["total"][h] == mv.sum()
         cstruct = cn / (qrows * FIX)
         assert pr["route"][h] == (1 if cstruct >= 0.1 else 0)
+        # every middle block of either direction holds exactly the same mass (B keys per
+        # proxy row), which equals the floor mu of Eq. 3, so the strict test of Eq. 4
+        # keeps nothing but the first and last block
+        nb = len(mv)
+        want = list(range(nb)) if nb <= 2 else [0, nb - 1]
+        assert oracle.vs_select(pr["mass_v"][h], pr["total"][h]).tolist() == want
+        assert oracle.vs_select(pr["mass_s"][h], pr["total"][h]).tolist() == want
 
 
 def test_proxy_matches_fp64_softmax(oracle_lib):
