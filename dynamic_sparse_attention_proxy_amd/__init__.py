@@ -22,7 +22,8 @@ STATUS = {0: "CRISP_OK", -1: "CRISP_ERR_NULL", -2: "CRISP_ERR_SHAPE", -3: "CRISP
           -8: "CRISP_ERR_ALIGN"}
 
 EXPORTS = ["crisp_workspace_size", "crisp_index_capacity", "crisp_route", "crisp_select_indices",
-           "crisp_sparse_prefill", "crisp_dense_prefill", "crisp_route_jsd", "crisp_status_string"]
+           "crisp_sparse_prefill", "crisp_dense_prefill", "crisp_route_jsd", "crisp_tile_layout_of",
+           "crisp_status_string"]
 
 
 class Shape(ctypes.Structure):
@@ -47,6 +48,11 @@ class IndexSets(ctypes.Structure):
                 ("mass_s", ctypes.c_void_p), ("mass_total", ctypes.c_void_p), ("vs_count", ctypes.c_void_p),
                 ("vs_vertical", ctypes.c_void_p), ("vs_slash", ctypes.c_void_p),
                 ("pe_rowptr", ctypes.c_void_p), ("pe_col", ctypes.c_void_p), ("pe_cap", ctypes.c_int64)]
+
+
+class TileLayout(ctypes.Structure):
+    _fields_ = [("list_offset", ctypes.c_int64), ("count_offset", ctypes.c_int64), ("list_stride", ctypes.c_int64),
+                ("n_lists", ctypes.c_int32), ("pair_lists", ctypes.c_int32)]
 
 
 class CrispError(RuntimeError):
@@ -87,6 +93,8 @@ def load_library(path: str = None):
         lib.crisp_route_jsd.argtypes = [S, C, ctypes.c_uint32, ctypes.c_uint32, P, P, ctypes.POINTER(IndexSets), P,
                                         ctypes.c_size_t, P, P, P, P]
         lib.crisp_route_jsd.restype = ctypes.c_int
+        lib.crisp_tile_layout_of.argtypes = [S, C, ctypes.POINTER(TileLayout)]
+        lib.crisp_tile_layout_of.restype = ctypes.c_int
         lib.crisp_status_string.argtypes = [ctypes.c_int]
         lib.crisp_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -277,6 +285,25 @@ def route_jsd(spec: LayerSpec, q, k, bufs: Buffers, route_out, jsd_out, tau_jsd=
     _check(load_library().crisp_route_jsd(ctypes.byref(spec.shape()), ctypes.byref(spec.config()), tau_jsd[0],
                                           tau_jsd[1], p["q"], p["k"], ctypes.byref(idx), bufs.ws.data_ptr(),
                                           bufs.ws_bytes, r_ptr, j_ptr, p_ptr, _stream(stream)), "crisp_route_jsd")
+
+
+def tile_layout(spec: LayerSpec) -> dict:
+    """crisp_tile_layout_of: where crisp_sparse_prefill keeps its key-tile lists inside the workspace."""
+    out = TileLayout()
+    _check(load_library().crisp_tile_layout_of(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
+                                               ctypes.byref(out)), "crisp_tile_layout_of")
+    return {name: int(getattr(out, name)) for name, _ in TileLayout._fields_}
+
+
+def tile_lists(spec: LayerSpec, bufs: Buffers):
+    """The key-tile lists the last crisp_sparse_prefill call left in ``bufs.ws``, as int32
+    device tensors (lists [n_lists, list_stride], counts [n_lists, N_b]) viewing the workspace."""
+    import torch
+    lay = tile_layout(spec)
+    n, stride, nb = lay["n_lists"], lay["list_stride"], spec.num_blocks
+    lists = bufs.ws[lay["list_offset"]: lay["list_offset"] + 4 * n * stride].view(torch.int32).view(n, stride)
+    counts = bufs.ws[lay["count_offset"]: lay["count_offset"] + 4 * n * nb].view(torch.int32).view(n, nb)
+    return lay, lists, counts
 
 
 def prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None, stream=None):

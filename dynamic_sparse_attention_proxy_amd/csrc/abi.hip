@@ -382,6 +382,20 @@ crisp_status crisp_route_jsd(const crisp_shape* shape, const crisp_config* cfg, 
   return hip_status();
 }
 
+crisp_status crisp_tile_layout_of(const crisp_shape* shape, const crisp_config* cfg, crisp_tile_layout* out) {
+  Dims d;
+  CRISP_TRY(make_dims(shape, cfg, &d));
+  if (!out) return CRISP_ERR_NULL;
+  const Layout L = layout(d);
+  const bool mat = use_matrix_engine(d);
+  out->list_offset = (int64_t)(mat ? L.a_ulist : L.a_tiles);
+  out->count_offset = (int64_t)(mat ? L.a_ucnt : L.a_cnt);
+  out->list_stride = d.ntri;
+  out->n_lists = mat ? d.bkv * ((d.group + 1) / 2) : d.bh;
+  out->pair_lists = mat ? 1 : 0;
+  return CRISP_OK;
+}
+
 const char* crisp_status_string(crisp_status s) {
   switch (s) {
     case CRISP_OK: return "ok";

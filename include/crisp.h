@@ -186,6 +186,37 @@ crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* c
                                  const void* k, const void* v, const crisp_rel_bias* bias, void* ws,
                                  size_t ws_bytes, void* o, void* stream);
 
+/* Where crisp_sparse_prefill keeps, inside ws, the key-tile lists it builds
+ * from the index sets: the per-query-block tile iterator of Alg. 1's attention
+ * step (summary page, Algorithm Overview), with the band rule of the selected
+ * slash blocks (Methodology, Alg. 3).  After the call's stream has completed
+ * the lists stay in ws until the next call that uses ws; this lets a caller
+ * inspect them.  For query block qb the list holds the key blocks kb <= qb
+ * that the attention visits, ascending, each with a mask mode:
+ *   1 lower triangle of the tile (r >= c: offsets (qb - kb) B + r - c in
+ *     slash block qb - kb, or the causal part of the diagonal tile),
+ *   2 upper triangle (r < c: slash block qb - kb - 1),
+ *   3 the whole tile (a vertical block, or a PE block below the diagonal).
+ * Layout: list_offset is the byte offset in ws of int32 [n_lists][list_stride]
+ * with the list of query block qb starting at element qb (qb + 1) / 2;
+ * count_offset the byte offset of int32 [n_lists][N_b], the list lengths.
+ * pair_lists = 1 (bf16, head_dim 128, block 128): one list per pair of query
+ * heads of a KV group, list l = kv * ceil(G / 2) + w for flattened KV head kv
+ * (batch * n_kv_heads + kv head) and pair w = query heads 2w, 2w + 1 of the
+ * group; entry = kb | mode(2w) << 24 | mode(2w + 1) << 26, a mode 0 where that
+ * head does not visit the tile (and for the missing second head of an odd G).
+ * pair_lists = 0 (other shapes): one list per flattened query head, entry =
+ * kb | mode << 28. */
+typedef struct {
+  int64_t list_offset;
+  int64_t count_offset;
+  int64_t list_stride; /* N_b (N_b + 1) / 2 */
+  int32_t n_lists;
+  int32_t pair_lists;
+} crisp_tile_layout;
+
+crisp_status crisp_tile_layout_of(const crisp_shape* shape, const crisp_config* cfg, crisp_tile_layout* out);
+
 /* The divergence router the pages contrast with C_struct (summary page,
  * Motivation: a second, pooled estimate of the head's attention, its
  * Jensen-Shannon divergence from the per-query one, VS above a threshold).

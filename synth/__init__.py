@@ -92,6 +92,7 @@ class Workload:
     slash_range: int = 4096
     fixed_slash: tuple = ()  # used instead of random draws when given
     fixed_verticals: tuple = ()  # key positions used instead of random draws when given
+    slash_bias: float = SLASH_BIAS  # nats added at each planted slash offset
     batch: int = 1
     qk_scale: float = 1.0  # power of two multiplying Q and K after rounding (0: all-zero Q and K)
     description: str = ""
@@ -243,7 +244,7 @@ def make_inputs(wl: Workload, with_v: bool = True, q_last_block_only: bool = Fal
     for b in range(wl.batch):
         for h, s in slashes.items():
             offs[b * wl.hq + h, : len(s)] = s
-            vals[b * wl.hq + h, : len(s)] = SLASH_BIAS
+            vals[b * wl.hq + h, : len(s)] = wl.slash_bias
     # heads without a planted slash get offsets that never occur (value 0 anyway)
     for r in range(bh):
         if count and not vals[r].any():

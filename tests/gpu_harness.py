@@ -138,3 +138,86 @@ class Timer:
 
     def __exit__(self, *a):
         log("done", self.what, f"{time.time() - self.t:.1f}s")
+
+
+def expected_tile_modes(head, nb):
+    """Mask mode of every causal key tile (qb, kb) of one head, from its index set:
+    3 for a selected vertical block or a PE block, 1 for the lower triangle of tile
+    qb - s and 2 for the upper triangle of tile qb - s - 1 of a selected slash block s,
+    the diagonal tile cut to its causal (lower) part; 0 where the head does not look."""
+    qb = np.arange(nb, dtype=np.int32)[:, None]
+    kb = np.arange(nb, dtype=np.int32)[None, :]
+    delta = qb - kb
+    M = np.zeros((nb, nb), np.uint8)
+    if head["route"]:
+        col = np.zeros(nb, bool)
+        col[np.asarray(head["vertical"], np.int64)] = True
+        sl = np.zeros(nb + 1, bool)
+        sl[np.asarray(head["slash"], np.int64)] = True
+        causal = delta >= 0
+        M[causal & col[None, :]] |= 3
+        M[causal & sl[np.clip(delta, 0, nb)]] |= 1
+        M[(delta >= 1) & sl[np.clip(delta - 1, 0, nb)]] |= 2
+    else:
+        rp = np.asarray(head["rowptr"], np.int64)
+        rows = np.repeat(np.arange(nb), np.diff(rp))
+        M[rows, np.asarray(head["cols"], np.int64)] = 3
+    d = np.arange(nb)
+    M[d, d] &= 1
+    return M
+
+
+def compare_tile_lists(spec, bufs, ref):
+    """The key-tile lists crisp_sparse_prefill left in the workspace against lists built
+    here from the oracle's index sets (ascending key blocks per query block, mask modes
+    per head).  Bit-exact; returns a list of mismatch strings."""
+    lay, lists, counts = crisp.tile_lists(spec, bufs)
+    nb = spec.num_blocks
+    G = spec.n_q_heads // spec.n_kv_heads
+    tri_r, tri_c = np.tril_indices(nb)
+    bad = []
+    if lay["pair_lists"]:
+        pairs = (G + 1) // 2
+        owners = []
+        for kv in range(spec.batch * spec.n_kv_heads):
+            b, g = divmod(kv, spec.n_kv_heads)
+            for w in range(pairs):
+                h0 = b * spec.n_q_heads + g * G + 2 * w
+                owners.append((h0, h0 + 1 if 2 * w + 1 < G else None))
+    else:
+        owners = [(h, None) for h in range(spec.heads)]
+    assert len(owners) == lay["n_lists"]
+    for li, (h0, h1) in enumerate(owners):
+        m0 = expected_tile_modes(ref["heads"][h0], nb)[tri_r, tri_c].astype(np.int32)
+        m1 = (expected_tile_modes(ref["heads"][h1], nb)[tri_r, tri_c].astype(np.int32) if h1 is not None
+              else np.zeros_like(m0))
+        keep = (m0 | m1) != 0
+        if lay["pair_lists"]:
+            want = (tri_c.astype(np.int32) | (m0 << 24) | (m1 << 26))[keep]
+        else:
+            want = (tri_c.astype(np.int32) | (m0 << 28))[keep]
+        want_cnt = np.bincount(tri_r[keep], minlength=nb)
+        got_cnt = counts[li].cpu().numpy()
+        if not np.array_equal(got_cnt, want_cnt):
+            d = np.argwhere(got_cnt != want_cnt).ravel()
+            bad.append(f"list {li} (heads {h0}, {h1}): counts differ at qb {d[:5].tolist()} "
+                       f"(gpu {got_cnt[d[:5]].tolist()} expected {want_cnt[d[:5]].tolist()})")
+            continue
+        got = lists[li].cpu().numpy()[tri_c < got_cnt[tri_r]]
+        if not np.array_equal(got, want):
+            d = np.argwhere(got != want).ravel()
+            bad.append(f"list {li} (heads {h0}, {h1}): {len(d)} entries differ, first {d[:3].tolist()}")
+    return bad
+
+
+def block_indicator_v(wl):
+    """Values that mark each key: the first d/2 columns one-hot on the key's block
+    (block index mod d/2), the last d/2 one-hot on its column (index mod d/2).  Exact in
+    bf16 and fp32."""
+    n, d, B = wl.n, wl.d, wl.block
+    half = d // 2
+    j = np.arange(n)
+    v = np.zeros((wl.batch * wl.hkv, n, d), np.float32)
+    v[:, j, (j // B) % half] = 1.0
+    v[:, j, half + j % half] = 1.0
+    return v

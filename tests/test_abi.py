@@ -169,3 +169,21 @@ def test_library_loads_after_torch():
             "c.load_library(); assert 'torch' in sys.modules; print('ok')")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
+
+
+def test_tile_layout(lib):
+    """Where crisp_sparse_prefill keeps its tile lists: pair lists for the matrix engine
+    (bf16, d 128, B 128), per-head lists otherwise, inside the workspace."""
+    s = _spec(n_q_heads=6, n_kv_heads=2)  # groups of 3: two pairs per KV head, the second with one head
+    lay = crisp.tile_layout(s)
+    nb = 8
+    assert lay["pair_lists"] == 1 and lay["n_lists"] == 2 * 2 and lay["list_stride"] == nb * (nb + 1) // 2
+    ws = crisp.workspace_size(s)
+    assert 0 <= lay["list_offset"] and lay["list_offset"] + 4 * lay["n_lists"] * lay["list_stride"] <= ws
+    assert lay["count_offset"] >= lay["list_offset"] + 4 * lay["n_lists"] * lay["list_stride"]
+    assert lay["count_offset"] + 4 * lay["n_lists"] * nb <= ws
+    g = crisp.tile_layout(_spec(dtype=crisp.F32, head_dim=64, block=64))
+    assert g["pair_lists"] == 0 and g["n_lists"] == 4 and g["list_stride"] == 16 * 17 // 2
+    assert lib.crisp_tile_layout_of(ctypes.byref(s.shape()), ctypes.byref(s.config()), None) == -1
+    with pytest.raises(crisp.CrispError, match="SHAPE"):
+        crisp.tile_layout(_spec(head_dim=96))

@@ -14,21 +14,25 @@ import pytest
 import dynamic_sparse_attention_proxy_amd as crisp
 import oracle
 import synth
-from gpu_harness import (DeviceInputs, Timer, compare_index_sets, download_index_sets, log, rows_of,
-                         run_dense, run_route_select, run_sparse, spec_for)
+from gpu_harness import (DeviceInputs, Timer, block_indicator_v, compare_index_sets, compare_tile_lists,
+                         download_index_sets, log, rows_of, run_dense, run_route_select, run_sparse, spec_for)
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 _cache = {}
+# the 512K noise-floor case (its oracle index sets take minutes) stays cached beside
+# the most recent other case, so the tests that reuse it need not follow one another
+_KEEP = ("llama_512k", crisp.SELECT_NOISE_FLOOR)
 
 
 def _case(name, wl=None, select_mode=crisp.SELECT_NOISE_FLOOR):
     key = (name, select_mode)
     if key in _cache:
         return _cache[key]
-    _cache.clear()
+    for other in [k for k in _cache if k != _KEEP]:
+        del _cache[other]
     gc.collect()
     wl = wl or synth.WORKLOADS[name]
     log("case", name, "mode", select_mode, "n", wl.n, "heads", wl.hq, wl.hkv, "d", wl.d, wl.dtype)
@@ -156,7 +160,76 @@ def test_index_sets_bit_exact(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ALL[::-1])  # the largest case is still cached from the test above
+@pytest.mark.parametrize("name", ["llama_512k", "tiny", "llama_32k", "qwen_128k"])
+def test_tile_lists_bit_exact(name):
+    """The key-tile lists of the attention step (index work) against lists built in the
+    test from the oracle's index sets: ascending key blocks per query block with each
+    head's mask mode (vertical block whole, slash band as the lower / upper triangles,
+    diagonal causal), bit for bit."""
+    wl, I, X, spec, bufs, ref = _case(name)
+    run_sparse(spec, X, bufs)
+    with Timer(f"tile lists {name}"):
+        bad = compare_tile_lists(spec, bufs, ref)
+    assert not bad, "\n".join(bad[:20])
+
+
+def _check_indicator_attention(wl, I, X, spec, bufs, ref, rows, heads, what):
+    """Attention on the real index sets with Q = 0, no bias and V marking each key's block
+    and column (block_indicator_v).  Every allowed key of a row then has probability
+    exactly 1/|allowed|: each output is a ratio of key counts, about 1/#tiles per block
+    class and 1/#keys per column class, so a dropped, doubled or misplaced tile, or a
+    mask edge one column off, moves outputs by far more than the bar.
+
+    Bar.  bf16 matrix engine: the scores are exactly 0, every probability is exactly 1
+    (also in bf16), the row sums and the products with V are sums of small integers in
+    fp32 (exact), so the only roundings are the reciprocal of the row sum, one product
+    and the final conversion to bf16: |o - o_exact| <= 2^-8 |o_exact| + 1e-6.  fp32
+    vector engine: the 1e-5 bar of every fp32 case (the roundings are the same, far
+    below it)."""
+    import torch
+    v_ind = block_indicator_v(wl)
+    dt = X.q.dtype
+    q0 = torch.zeros_like(X.q)
+    v_dev = torch.from_numpy(v_ind).cuda().to(dt).contiguous()
+    hsel = torch.as_tensor(heads, device="cuda")
+    o = torch.empty_like(X.q)
+    crisp.sparse_prefill(spec, q0, X.k, v_dev, o, bufs)
+    od = torch.empty_like(X.q)
+    crisp.dense_prefill(spec, q0, X.k, v_dev, od, bufs)
+    torch.cuda.synchronize()
+    o_sp, o_de = rows_of(o[hsel], rows), rows_of(od[hsel], rows)
+    del q0, v_dev, o, od
+    zq = np.broadcast_to(np.float32(0.0), I.q.shape)
+    specs = oracle.specs_from_index_sets(ref)
+    with Timer(f"oracle indicator attention {what}"):
+        r_sp = oracle.attention(zq, I.k, v_ind, wl.block, specs, rows=rows, heads=heads, chunk=512)
+        r_de = oracle.attention(zq, I.k, v_ind, wl.block, [dict(kind="dense")] * len(specs), rows=rows,
+                                heads=heads, chunk=512)
+    for got, want, kind in ((o_sp, r_sp, "sparse"), (o_de, r_de, "dense")):
+        err = np.abs(got - want)
+        bar = TOL["f32"] if wl.dtype == "f32" else 2.0 ** -8 * np.abs(want) + 1e-6
+        log(what, kind, "max-abs", float(err.max()), "max err/bar", float((err / bar).max()))
+        assert np.all(err <= bar), f"{kind}: worst {np.unravel_index(np.argmax(err / bar), err.shape)}"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama_512k", "tiny", "llama_32k", "gqa3_bf16"])
+def test_attention_block_indicator(name):
+    if name in EDGE:
+        wl, I, X, spec, bufs, ref = _case("edge_" + name, EDGE[name])
+    else:
+        wl, I, X, spec, bufs, ref = _case(name)
+    if name == "llama_512k":
+        rows, heads = synth.sample_rows(wl), list(range(wl.hq))
+    elif name == "llama_32k":
+        rows, heads = None, [0, 1, 16, 17]
+    else:
+        rows, heads = None, list(range(wl.hq))
+    _check_indicator_attention(wl, I, X, spec, bufs, ref, rows, heads, f"{name} indicator")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ALL[::-1])
 def test_jsd_router(name):
     """The divergence router bit-exact against the oracle; on the planted layers it makes
     the same decisions as C_struct (planted heads diverge from their pooled estimate)."""
@@ -193,13 +266,75 @@ def test_cumulative_mode(name):
     _check_attention(wl, I, X, spec, bufs, ref, rows, f"{name} cumulative")
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
+def test_cumulative_mode_multichunk_512k():
+    """N_b = 4096: the cumulative-coverage kernel runs its radix passes and its
+    compaction over four chunks of 1024 blocks, carrying the tie count across chunks.
+    VS lists bit-exact against the oracle's cumulative rule on the oracle's masses
+    (which the GPU's equal bit for bit); PE index sets as in the noise-floor mode;
+    attention on the new sets within the bar on 256 sampled rows of eight heads."""
+    import dataclasses
+    wl, I, X, spec, bufs, ref = _case("llama_512k")
+    spec_c = dataclasses.replace(spec, select_mode=crisp.SELECT_CUMULATIVE)
+    with Timer("gpu route+select 512k cumulative"):
+        b2 = run_route_select(spec_c, X)
+    gpu = download_index_sets(b2)
+    pr = ref["proxy"]
+    cum = {"proxy": pr, "heads": []}
+    for h in range(wl.hq):
+        if pr["route"][h]:
+            cum["heads"].append(dict(route=1, vertical=oracle.cumulative_select(pr["mass_v"][h], pr["total"][h],
+                                                                                synth.GAMMA),
+                                     slash=oracle.cumulative_select(pr["mass_s"][h], pr["total"][h], synth.GAMMA)))
+        else:
+            cum["heads"].append(ref["heads"][h])
+    bad = compare_index_sets(gpu, cum)
+    assert not bad, "\n".join(bad[:20])
+    nv = [len(cum["heads"][h]["vertical"]) for h in range(wl.hq) if pr["route"][h]]
+    log("512k cumulative vertical blocks per VS head", nv)
+    assert min(nv) > 1024  # the selected lists themselves span several chunks
+    heads = [0, 1, 2, 3, 16, 17, 18, 19]
+    _check_attention(wl, I, X, spec_c, b2, cum, synth.sample_rows(wl), "512k cumulative", heads=heads)
+
+
+# Every middle block ties (Q = K = 0), and one head carries a 12-nat bias on the main
+# diagonal, enough mass at the anchor positions to route it to VS but not enough to
+# reach gamma = 0.95 alone: the cumulative cut falls inside the run of tied blocks,
+# at about tie rank 1300 of 1500, past the first 1024-block chunk.  Fp32, d 64, B 64,
+# n = 95990 (N_b = 1500, a ragged last block of 54 rows).  The other head is uniform
+# and routes to PE, whose pooled map is then one big tie as well.
+TIES = synth.Workload(name="cumulative_ties", hq=2, hkv=1, d=64, n=95990, dtype="f32", block=64, rope_theta=0.0,
+                      seed=46, planted_heads=[0], n_vertical=0, fixed_slash=(0,), slash_bias=12.0, qk_scale=0.0)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", [crisp.SELECT_CUMULATIVE, crisp.SELECT_NOISE_FLOOR])
+def test_ties_across_chunks(mode):
+    wl, I, X, spec, bufs, ref = _case("ties", TIES, mode)
+    gpu = download_index_sets(bufs)
+    bad = compare_index_sets(gpu, ref)
+    assert not bad, "\n".join(bad[:20])
+    assert gpu["route"].tolist() == [1, 0]
+    nb = spec.num_blocks
+    h0 = ref["heads"][0]
+    if mode == crisp.SELECT_CUMULATIVE:
+        for key in ("vertical", "slash"):
+            sel = np.asarray(h0[key])
+            log("ties", key, "selected", len(sel))
+            assert 1024 < len(sel) < nb - 1, (key, len(sel))
+    else:
+        assert h0["vertical"].tolist() == [0, nb - 1] and h0["slash"].tolist() == [0, nb - 1]
+    _check_attention(wl, I, X, spec, bufs, ref, synth.sample_rows(wl), f"ties mode {mode}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama_32k", "llama_512k"])
 @pytest.mark.parametrize("alpha", [(5, 4), (3, 2)])
-def test_alpha_variants(alpha):
+def test_alpha_variants(alpha, name):
     """Eq. 4 with the pages' larger multipliers: VS lists bit-exact against the oracle on the
     same (bit-exact) masses; a larger alpha never keeps more blocks."""
     import dataclasses
-    wl, I, X, spec, bufs, ref = _case("llama_32k")
+    wl, I, X, spec, bufs, ref = _case(name)
     spec_a = dataclasses.replace(spec, alpha=alpha)
     b2 = run_route_select(spec_a, X)
     gpu = download_index_sets(b2)
@@ -214,17 +349,19 @@ def test_alpha_variants(alpha):
             assert set(want.tolist()) <= set(base["heads"][h][key].tolist()), (h, key)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama_32k", "llama_512k"])
 @pytest.mark.parametrize("mode", [crisp.SELECT_NOISE_FLOOR, crisp.SELECT_CUMULATIVE])
-def test_gamma_variant(mode):
+def test_gamma_variant(mode, name):
     """gamma = 97/100, the pages' wider coverage: PE index sets (and, in the cumulative mode,
     the VS lists) bit-exact against the oracle; a larger gamma never keeps fewer blocks."""
     import dataclasses
-    wl, I, X, spec, bufs, ref = _case("llama_32k", select_mode=mode)
-    spec_g = dataclasses.replace(spec, gamma=(97, 100))
+    wl, I, X, spec, bufs, ref = _case(name)
+    spec_b = dataclasses.replace(spec, select_mode=mode)
+    spec_g = dataclasses.replace(spec_b, gamma=(97, 100))
+    base = download_index_sets(run_route_select(spec_b, X))
     b2 = run_route_select(spec_g, X)
     gpu = download_index_sets(b2)
-    base = download_index_sets(bufs)
     pr = ref["proxy"]
     G = wl.hq // wl.hkv
     assert np.array_equal(gpu["route"], pr["route"])
