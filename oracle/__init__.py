@@ -46,9 +46,11 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        # CRISP_ORACLE_LIB: another build of the same source (the sanitizer test loads one)
+        path = os.environ.get("CRISP_ORACLE_LIB") or _LIB_PATH
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         P, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
         lib.oracle_exp_crisp.argtypes = [ctypes.c_float]
         lib.oracle_exp_crisp.restype = ctypes.c_float

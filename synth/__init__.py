@@ -54,9 +54,11 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        # CRISP_SYNTH_LIB: another build of the same source (the sanitizer test loads one)
+        path = os.environ.get("CRISP_SYNTH_LIB") or _LIB_PATH
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         lib.synth_fill.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_uint64, ctypes.c_uint32, ctypes.c_double, ctypes.c_double, P, P, P,
