@@ -19,11 +19,11 @@ SELECT_NOISE_FLOOR, SELECT_KEEP_ALL, SELECT_CUMULATIVE = 0, 1, 2
 
 STATUS = {0: "CRISP_OK", -1: "CRISP_ERR_NULL", -2: "CRISP_ERR_SHAPE", -3: "CRISP_ERR_DTYPE",
           -4: "CRISP_ERR_CONFIG", -5: "CRISP_ERR_WORKSPACE", -6: "CRISP_ERR_CAPACITY", -7: "CRISP_ERR_HIP",
-          -8: "CRISP_ERR_ALIGN"}
+          -8: "CRISP_ERR_ALIGN", -9: "CRISP_ERR_SCRATCH"}
 
 EXPORTS = ["crisp_workspace_size", "crisp_index_capacity", "crisp_route", "crisp_select_indices",
-           "crisp_sparse_prefill", "crisp_dense_prefill", "crisp_route_jsd", "crisp_tile_layout_of",
-           "crisp_status_string"]
+           "crisp_sparse_prefill", "crisp_sparse_prefill_noalloc", "crisp_dense_prefill", "crisp_route_jsd",
+           "crisp_tile_layout_of", "crisp_status_string"]
 
 
 class Shape(ctypes.Structure):
@@ -88,6 +88,9 @@ def load_library(path: str = None):
         lib.crisp_sparse_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), ctypes.POINTER(IndexSets), P,
                                              ctypes.c_size_t, P, P]
         lib.crisp_sparse_prefill.restype = ctypes.c_int
+        lib.crisp_sparse_prefill_noalloc.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias),
+                                                     ctypes.POINTER(IndexSets), P, P]
+        lib.crisp_sparse_prefill_noalloc.restype = ctypes.c_int
         lib.crisp_dense_prefill.argtypes = [S, C, P, P, P, ctypes.POINTER(RelBias), P, ctypes.c_size_t, P, P]
         lib.crisp_dense_prefill.restype = ctypes.c_int
         lib.crisp_route_jsd.argtypes = [S, C, ctypes.c_uint32, ctypes.c_uint32, P, P, ctypes.POINTER(IndexSets), P,
@@ -258,6 +261,18 @@ def sparse_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None
                                                p["k"], p["v"], ctypes.byref(b), ctypes.byref(idx),
                                                bufs.ws.data_ptr(), bufs.ws_bytes, p["o"], _stream(stream)),
            "crisp_sparse_prefill")
+
+
+def sparse_prefill_noalloc(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None,
+                           stream=None):
+    """crisp_sparse_prefill_noalloc: the same attention with the library's static scratch
+    (no workspace; ``bufs`` supplies only the index sets)."""
+    idx = bufs.index_sets()
+    b = _bias(spec, bias_offsets, bias_values)
+    p = _qkvo(spec, q=q, k=k, v=v, o=o)
+    _check(load_library().crisp_sparse_prefill_noalloc(ctypes.byref(spec.shape()), ctypes.byref(spec.config()),
+                                                       p["q"], p["k"], p["v"], ctypes.byref(b), ctypes.byref(idx),
+                                                       p["o"], _stream(stream)), "crisp_sparse_prefill_noalloc")
 
 
 def dense_prefill(spec: LayerSpec, q, k, v, o, bufs: Buffers, bias_offsets=None, bias_values=None,

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/crisp.h"
 #include "kernels.h"
 
@@ -213,6 +215,67 @@ crisp_status hip_status() {
     if (s_ != CRISP_OK) return s_;   \
   } while (0)
 
+// Argument checks shared by the two sparse-prefill entry points.
+crisp_status check_sparse_args(const crisp_shape* shape, const crisp_config* cfg, const void* q, const void* k,
+                               const void* v, const crisp_rel_bias* bias, const crisp_index_sets* idx,
+                               const void* o, Dims* d, BiasArgs* ba) {
+  CRISP_TRY(make_dims(shape, cfg, d));
+  CRISP_TRY(check_tensor(q));
+  CRISP_TRY(check_tensor(k));
+  CRISP_TRY(check_tensor(v));
+  CRISP_TRY(check_tensor(o));
+  if (!idx || !idx->route) return CRISP_ERR_NULL;
+  CRISP_TRY(check_list_fields(idx, *d));
+  CRISP_TRY(check_bias(bias, ba));
+  return CRISP_OK;
+}
+
+// Tile lists, then attention, with the scratch regions carved from w.
+crisp_status run_sparse(const Dims& d, const Layout& L, const BiasArgs& ba, const void* q, const void* k,
+                        const void* v, const crisp_index_sets* idx, char* w, void* o, void* stream) {
+  int* tiles = reinterpret_cast<int*>(w + L.a_tiles);
+  int* cnt = reinterpret_cast<int*>(w + L.a_cnt);
+  int* ulist = reinterpret_cast<int*>(w + L.a_ulist);
+  int* ucnt = reinterpret_cast<int*>(w + L.a_ucnt);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (launch_build_tiles(d, index_out(idx), tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
+  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, w + L.a_vt,
+                       reinterpret_cast<int*>(w + L.a_qcnt), reinterpret_cast<float*>(w + L.a_part),
+                       st) != hipSuccess)
+    return CRISP_ERR_HIP;
+  return hip_status();
+}
+
+// Scratch of crisp_sparse_prefill_noalloc: a static device array, one copy per
+// GPU the library runs on.  Host code never passes the array's name to a
+// kernel (on the host it only names the symbol): the device address of each
+// GPU's copy is looked up once per device with hipGetSymbolAddress, with that
+// device current, and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+crisp_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CRISP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CRISP_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return CRISP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -301,31 +364,26 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
                                   const crisp_index_sets* idx, void* ws, size_t ws_bytes, void* o,
                                   void* stream) {
   Dims d;
-  CRISP_TRY(make_dims(shape, cfg, &d));
-  CRISP_TRY(check_tensor(q));
-  CRISP_TRY(check_tensor(k));
-  CRISP_TRY(check_tensor(v));
-  CRISP_TRY(check_tensor(o));
-  CRISP_TRY(check_tensor(ws));
-  if (!idx || !idx->route) return CRISP_ERR_NULL;
-  CRISP_TRY(check_list_fields(idx, d));
   BiasArgs ba;
-  CRISP_TRY(check_bias(bias, &ba));
+  CRISP_TRY(check_sparse_args(shape, cfg, q, k, v, bias, idx, o, &d, &ba));
+  CRISP_TRY(check_tensor(ws));
   const Layout L = layout(d);
   if (ws_bytes < L.total) return CRISP_ERR_WORKSPACE;
-  char* w = static_cast<char*>(ws);
-  int* tiles = reinterpret_cast<int*>(w + L.a_tiles);
-  int* cnt = reinterpret_cast<int*>(w + L.a_cnt);
-  int* ulist = reinterpret_cast<int*>(w + L.a_ulist);
-  int* ucnt = reinterpret_cast<int*>(w + L.a_ucnt);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  if (launch_build_tiles(d, index_out(idx), tiles, cnt, ulist, ucnt, st) != hipSuccess) return CRISP_ERR_HIP;
-  if (launch_attention(d, ba, q, k, v, o, tiles, cnt, ulist, ucnt, w + L.a_vt,
-                       reinterpret_cast<int*>(w + L.a_qcnt), reinterpret_cast<float*>(w + L.a_part),
-                       st) != hipSuccess)
-    return CRISP_ERR_HIP;
-  return hip_status();
+  return run_sparse(d, L, ba, q, k, v, idx, static_cast<char*>(ws), o, stream);
+}
+
+crisp_status crisp_sparse_prefill_noalloc(const crisp_shape* shape, const crisp_config* cfg, const void* q,
+                                          const void* k, const void* v, const crisp_rel_bias* bias,
+                                          const crisp_index_sets* idx, void* o, void* stream) {
+  Dims d;
+  BiasArgs ba;
+  CRISP_TRY(check_sparse_args(shape, cfg, q, k, v, bias, idx, o, &d, &ba));
+  const Layout L = layout(d);
+  // the attention regions of the layout start at offset 0 and end at a_end
+  if (L.a_end > kScratchBytes) return CRISP_ERR_SCRATCH;
+  void* sp = nullptr;
+  CRISP_TRY(device_scratch(&sp));
+  return run_sparse(d, L, ba, q, k, v, idx, static_cast<char*>(sp), o, stream);
 }
 
 crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
@@ -407,6 +465,7 @@ const char* crisp_status_string(crisp_status s) {
     case CRISP_ERR_CAPACITY: return "index capacity too small";
     case CRISP_ERR_HIP: return "HIP launch failed";
     case CRISP_ERR_ALIGN: return "pointer not aligned";
+    case CRISP_ERR_SCRATCH: return "problem needs more scratch than the allocation-free entry point holds (128 MiB)";
   }
   return "unknown status";
 }

@@ -74,7 +74,8 @@ typedef enum {
   CRISP_ERR_WORKSPACE = -5, /* ws_bytes < crisp_workspace_size() */
   CRISP_ERR_CAPACITY = -6,  /* pe_cap < crisp_index_capacity() */
   CRISP_ERR_HIP = -7,       /* a HIP launch failed */
-  CRISP_ERR_ALIGN = -8      /* a pointer is not 16-byte aligned */
+  CRISP_ERR_ALIGN = -8,     /* a pointer is not 16-byte aligned */
+  CRISP_ERR_SCRATCH = -9    /* crisp_sparse_prefill_noalloc: the problem exceeds its static scratch */
 } crisp_status;
 
 typedef enum { CRISP_F32 = 0, CRISP_BF16 = 1 } crisp_dtype;
@@ -185,6 +186,25 @@ crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* 
 crisp_status crisp_dense_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
                                  const void* k, const void* v, const crisp_rel_bias* bias, void* ws,
                                  size_t ws_bytes, void* o, void* stream);
+
+/* crisp_sparse_prefill without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory around the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same operation, arguments, kernels and results (bit for bit) as
+ * crisp_sparse_prefill; its scratch (key-tile lists, V^T, work-queue counters)
+ * lives in a static device array of 128 MiB that the library holds on every
+ * GPU it runs on until the process ends.  Problems whose attention scratch
+ * exceeds 128 MiB are refused with CRISP_ERR_SCRATCH before anything is
+ * enqueued: with bf16, head_dim 128 and block 128 the scratch is about
+ * 2 * n_kv_heads * head_dim * seq_len bytes (V^T) plus the tile lists, so
+ * 8 KV heads fit up to about 60K tokens.  The array keeps the last call's
+ * contents; every call writes all it reads.  Calls share the one array per
+ * GPU: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  The first call on a
+ * device looks up that device's copy of the array (no allocation). */
+crisp_status crisp_sparse_prefill_noalloc(const crisp_shape* shape, const crisp_config* cfg, const void* q,
+                                          const void* k, const void* v, const crisp_rel_bias* bias,
+                                          const crisp_index_sets* idx, void* o, void* stream);
 
 /* Where crisp_sparse_prefill keeps, inside ws, the key-tile lists it builds
  * from the index sets: the per-query-block tile iterator of Alg. 1's attention

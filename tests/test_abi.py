@@ -136,7 +136,7 @@ def test_select_modes(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert lib.crisp_status_string(code)
     assert lib.crisp_status_string(-99) == b"unknown status"
 
@@ -187,3 +187,27 @@ def test_tile_layout(lib):
     assert lib.crisp_tile_layout_of(ctypes.byref(s.shape()), ctypes.byref(s.config()), None) == -1
     with pytest.raises(crisp.CrispError, match="SHAPE"):
         crisp.tile_layout(_spec(head_dim=96))
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free entry point: the same argument checks as crisp_sparse_prefill, and a
+    problem whose attention scratch exceeds its static array is refused (no launch is reached)."""
+    f = lib.crisp_sparse_prefill_noalloc
+    s = _spec()
+    sh, cf = ctypes.byref(s.shape()), ctypes.byref(s.config())
+    fake = ctypes.c_void_p(1 << 20)
+    idx = crisp.IndexSets(*([1 << 20] * 10), crisp.index_capacity(s))
+    assert f(sh, cf, None, fake, fake, None, ctypes.byref(idx), fake, None) == -1
+    assert f(sh, cf, fake, fake, fake, None, None, fake, None) == -1
+    assert f(sh, cf, fake, fake, fake, None, ctypes.byref(idx), ctypes.c_void_p((1 << 20) + 2), None) == -8
+    small = crisp.IndexSets(*([1 << 20] * 10), crisp.index_capacity(s) - 1)
+    assert f(sh, cf, fake, fake, fake, None, ctypes.byref(small), fake, None) == -6
+    bad = _spec(head_dim=96)
+    assert f(ctypes.byref(bad.shape()), ctypes.byref(bad.config()), fake, fake, fake, None, ctypes.byref(idx), fake,
+             None) == -2
+    # a Llama-shaped 128K layer: V^T of 8 KV heads alone is 256 MiB
+    big = _spec(n_q_heads=32, n_kv_heads=8, seq_len=131072)
+    bidx = crisp.IndexSets(*([1 << 20] * 10), crisp.index_capacity(big))
+    assert f(ctypes.byref(big.shape()), ctypes.byref(big.config()), fake, fake, fake, None, ctypes.byref(bidx), fake,
+             None) == -9
+    assert b"128 MiB" in lib.crisp_status_string(-9)
