@@ -307,6 +307,27 @@ def param_sweep(names=("llama_128k", "llama_512k")):
     return out
 
 
+def next_rows():
+    """The comparison rows in brief: the noise floor against the cumulative-coverage rule at
+    128K and 512K, and the pages' other alpha and gamma at 512K (selected blocks per
+    direction over the VS heads, tile densities, route + select and attention times)."""
+    import torch
+
+    import dynamic_sparse_attention_proxy_amd as crisp
+    import synth
+    out = {}
+    for name, variants in (("llama_128k", (("noise_floor", {}), ("cumulative", {"select_mode": crisp.SELECT_CUMULATIVE}))),
+                           ("llama_512k", (("noise_floor", {}), ("cumulative", {"select_mode": crisp.SELECT_CUMULATIVE}),
+                                           ("alpha=3/2", {"alpha": (3, 2)}), ("gamma=97/100", {"gamma": (97, 100)})))):
+        wl = synth.WORKLOADS[name]
+        X = _device_layer(wl)
+        out[name] = {label: _variant_stats(wl, X, **ov) for label, ov in variants}
+        log(f"next rows {name}: {out[name]}")
+        del X
+        torch.cuda.empty_cache()
+    return out
+
+
 def per_config(names=("tiny", "llama_32k", "llama_128k", "qwen_128k", "llama_512k")):
     """Stage times, own dense time, speedup and densities of every workload (3 steps)."""
     import torch
@@ -345,7 +366,7 @@ def copy_calibration(gib: float = 4.0):
     print(json.dumps({"copy_bytes": n, "reps": 3}))
 
 
-def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
+def measure(wl, steps, warmup, with_dense=True, dense_reps=None, sampler=None):
     import torch
 
     import dynamic_sparse_attention_proxy_amd as crisp
@@ -387,6 +408,7 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
     stage = {"route": [], "select": [], "attention": []}
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
+    wall0 = time.time()
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
@@ -398,11 +420,13 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
         ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = sampler.window(wall0, time.time()) if sampler is not None else None
     for i in range(steps):
         stage["route"].append(ev[i][0].elapsed_time(ev[i][1]))
         stage["select"].append(ev[i][1].elapsed_time(ev[i][2]))
         stage["attention"].append(ev[i][2].elapsed_time(ev[i][3]))
-    res = {"I": I, "spec": spec, "bufs": bufs, "wall_s": wall,
+    res = {"I": I, "spec": spec, "bufs": bufs, "wall_s": wall, "clock": clock,
+           "stage_bytes": stage_bytes(wl, bufs),
            "stage_ms": {kk: sum(vv) / len(vv) for kk, vv in stage.items()}}
     if with_dense:
         od = torch.empty_like(q)
@@ -427,6 +451,98 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None):
     return res
 
 
+def stage_bytes(wl, bufs=None):
+    """Bytes the routing and selection stages move by design (their traffic model), for
+    their HBM fractions.  Route: K read once per KV head and the last query block of every
+    head, the proxy scores S written once and streamed twice (row sums, then masses), the
+    per-block partials.  Select (PE heads only): Q of the PE heads and K of their KV groups
+    read once for the block means, the pooled map written once (8 B per entry) and read
+    by the four radix passes, the row counts and the CSR writer (six reads)."""
+    import numpy as np
+    B, d, n = wl.block, wl.d, wl.n
+    nb = (n + B - 1) // B
+    bh, bkv = wl.batch * wl.hq, wl.batch * wl.hkv
+    esz = 2 if wl.dtype == "bf16" else 4
+    s_bytes = bh * nb * B * B * 4
+    route = bkv * n * d * esz + bh * B * d * esz + 3 * s_bytes + 4 * bh * nb * 8
+    if bufs is None:
+        return {"route": route}
+    vs = bufs.route.cpu().numpy().astype(bool)
+    n_pe = int((~vs).sum())
+    G = wl.hq // wl.hkv
+    pe_groups = len({h // G for h in np.nonzero(~vs)[0]})
+    ntri = nb * (nb + 1) // 2
+    select = n_pe * n * d * esz + pe_groups * n * d * esz + n_pe * ntri * 8 * (1 + 6)
+    return {"route": route, "select": select}
+
+
+class ClockSampler:
+    """Read-only samples of the GPU clock and board power: a shell loop running
+    `amd-smi metric --power --clock` about every 0.3 s, started before this process
+    touches the GPU (a process that has initialised the GPU does not start other
+    programs), stopped by its process group at the end.  Nothing is changed on the
+    device."""
+
+    def __init__(self):
+        import subprocess
+        import tempfile
+        self.path = tempfile.mktemp(prefix="crisp_amdsmi_", suffix=".txt")
+        self.proc = None
+        try:
+            self.out = open(self.path, "w")
+            self.proc = subprocess.Popen(
+                ["bash", "-c", "while :; do echo \"@@ $(date +%s.%N)\"; amd-smi metric --power --clock; sleep 0.3; done"],
+                stdout=self.out, stderr=subprocess.DEVNULL, start_new_session=True)
+        except OSError:
+            self.proc = None
+
+    def stop(self):
+        import signal
+        if self.proc is not None and self.proc.poll() is None:
+            try:
+                os.killpg(self.proc.pid, signal.SIGTERM)
+            except OSError:
+                pass
+            self.proc.wait(timeout=10)
+        if self.proc is not None:
+            self.out.close()
+
+    def window(self, t0, t1):
+        """Clock and power samples taken between wall times t0 and t1 (seconds)."""
+        if self.proc is None or not os.path.exists(self.path):
+            return None
+        with open(self.path) as f:
+            text = f.read()
+        keep = []
+        for chunk in text.split("@@ ")[1:]:
+            head, _, body = chunk.partition("\n")
+            try:
+                ts = float(head.strip())
+            except ValueError:
+                continue
+            if t0 <= ts <= t1:
+                keep.append(body)
+        return parse_amd_smi(keep)
+
+
+def parse_amd_smi(samples):
+    """GFX clock (MHz) and socket power (W) from `amd-smi metric --power --clock` text."""
+    import re
+    clocks, power = [], []
+    for text in samples:
+        # GFX_0 .. GFX_7 sections, each with CLK: <n> MHz; the power section has SOCKET_POWER: <n> W
+        for m in re.finditer(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text):
+            clocks.append(float(m.group(1)))
+        for m in re.finditer(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text):
+            power.append(float(m.group(1)))
+    if not clocks:
+        return None
+    import statistics
+    return {"gfx_mhz_mean": round(statistics.fmean(clocks), 1), "gfx_mhz_min": min(clocks),
+            "gfx_mhz_max": max(clocks), "socket_power_w_median": statistics.median(power) if power else None,
+            "samples": len(samples)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,6 +553,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K speedup side measurement")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the compact noise-floor / cumulative / alpha / gamma comparison at 128K and 512K")
     ap.add_argument("--selection-sweep", action="store_true",
                     help="add the noise-floor vs cumulative-coverage budget over 32K/128K/512K and the Qwen-shaped 128K layer")
     ap.add_argument("--per-config", action="store_true",
@@ -455,8 +573,12 @@ def main():
         return
     import synth
     wl = synth.WORKLOADS[args.config]
+    sampler = ClockSampler()  # before the first GPU call of this process
     torch.cuda.set_device(0)
-    r = measure(wl, args.steps, args.warmup, with_dense=not args.no_dense)
+    try:
+        r = measure(wl, args.steps, args.warmup, with_dense=not args.no_dense, sampler=sampler)
+    finally:
+        sampler.stop()
     st = r["stage_ms"]
     total_ms = st["route"] + st["select"] + st["attention"]
     tiles = sum(r["tiles"])
@@ -494,11 +616,30 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel (crisp_sparse_prefill launch)",
                      "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops, "flops_basis": "computed tiles x 4 d B^2"},
         "context": {"pages_attention_speedup_512k": "up to 5.30x (summary, real model maps); 5.17x-5.40x "
                                                     "attention-only over FlashAttention on a single H100 "
                                                     "(Table 4)"},
     }
+    rl = out["roofline"]
+    if r["pair_density"] is not None:
+        useful = r["pair_density"] * wl.batch * wl.hq * 4.0 * d * wl.n * (wl.n + 1) / 2
+        rl["useful_flops_per_launch"] = useful
+        rl["achieved_useful"] = round(useful / (st["attention"] * 1e-3) / 1e12, 1)
+        rl["frac_useful"] = round(rl["achieved_useful"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    if r["clock"]:
+        # the published peak is quoted at 2.4 GHz; under this load the board's power cap
+        # holds a lower clock, sampled read-only during the timed steps
+        ck = r["clock"]
+        rl["clock"] = ck
+        rl["frac_of_peak_at_held_clock"] = round(achieved / (MFMA_BF16_PEAK_TFLOPS * ck["gfx_mhz_mean"] / 2400.0), 4)
+    out["hbm_stages"] = {
+        k2: {"bytes": r["stage_bytes"][k2], "ms": round(st[k2], 3),
+             "gb_per_s": round(r["stage_bytes"][k2] / (st[k2] * 1e-3) / 1e9, 1),
+             "frac": round(r["stage_bytes"][k2] / (st[k2] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "peak_gb_per_s": HBM_PEAK_GBS}
+        for k2 in ("route", "select") if k2 in r["stage_bytes"]}
+    out["hbm_stages"]["note"] = ("stage time includes every kernel of the call; route's proxy-score kernel is "
+                                 "bound by the fp32 vector ALU; per-kernel figures in profiles/")
     out["jsd_router"] = dict(r["jsd_router"], cstruct_router_ms=round(st["route"], 3),
                              note="route = proxy map + block masses + C_struct; the divergence router needs "
                                   "the same proxy plus extra_ms (block means, pooled row, softmax, JSD)")
@@ -516,6 +657,8 @@ def main():
                           "speedup_vs_dense": round(r2["dense_ms"] / tot2, 3),
                           "stage_ms": {kk: round(vv, 3) for kk, vv in st2.items()}}
         del r2
+    if not args.no_next and args.config == "llama_512k":
+        out["next_rows"] = next_rows()
     if args.selection_sweep:
         out["selection_sweep"] = selection_sweep()
     if args.param_sweep:

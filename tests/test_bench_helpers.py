@@ -84,3 +84,29 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode != 0
     assert "--gpus 1" in r.stderr
     assert not r.stdout.strip()
+
+
+def test_amd_smi_parse():
+    """The clock / power sampler reads amd-smi's text output (format as printed by
+    `amd-smi metric --power --clock` on an MI355X machine, trimmed)."""
+    import bench
+    text = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1383 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 2047 MHz
+            MIN_CLK: 157 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 2101 MHz
+            MIN_CLK: 157 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 2000 MHz
+"""
+    r = bench.parse_amd_smi([text, text.replace("1383", "1371")])
+    assert r["gfx_mhz_min"] == 2047 and r["gfx_mhz_max"] == 2101 and r["gfx_mhz_mean"] == 2074.0
+    assert r["socket_power_w_median"] == 1377.0 and r["samples"] == 2
+    assert bench.parse_amd_smi(["AMDSMI Tool: no GPU"]) is None
