@@ -54,12 +54,13 @@ __device__ __forceinline__ void mean8(const T* p, int d, int cnt, float* out) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = 0.0f;
   int r = 0;
-  for (; r + 4 <= cnt; r += 4) {
-    float x[4][8];
+  // eight rows' loads in flight before their (sequential) sums
+  for (; r + 8 <= cnt; r += 8) {
+    float x[8][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load8(p + (size_t)(r + j) * d, x[j]);
+    for (int j = 0; j < 8; ++j) load8(p + (size_t)(r + j) * d, x[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = s[i] + x[j][i];
   }

@@ -196,57 +196,104 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(Dims dm, const T* __restri
   o4[1] = make_float4(out[4], out[5], out[6], out[7]);
 }
 
-// Pooled scores, 64 x 64 tile per block, 4 x 4 per thread, chunk of 32 over d.
+// Pooled scores zbar[qb][kb] = fl(fma-chain(Qbar_qb, Kbar_kb) c) for kb <= qb, one
+// 128 x 128 tile of (query block, key block) per workgroup (tiles on or below the
+// diagonal only), 8 x 8 per thread.  The head dimension is staged through LDS in
+// 32-wide chunks: each thread reads 16-byte pieces of the rows, held in registers
+// while the previous chunk is computed, and stores them dim-major so that a thread
+// reads its 8 rows (and 8 keys) of one dimension as two 16-byte LDS loads.  Every
+// accumulator keeps its fma chain over the dimensions in ascending order.
+constexpr int kPsTile = 128, kPsTm = 8, kPsKc = 32, kPsLd = kPsTile + 4;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void pe_scores_kernel(Dims dm, IndexOut io,
                                                              const float* __restrict__ qbar,
                                                              const float* __restrict__ kbar,
                                                              float* __restrict__ zbar) {
-  constexpr int TL = 64, TM = 4, KC = 32, LD = TL + 4;
-  __shared__ __align__(16) float Qs[KC * LD];
-  __shared__ __align__(16) float Ks[KC * LD];
-  const int rt = blockIdx.x, ct = blockIdx.y, bh = blockIdx.z, tid = threadIdx.x;
-  if (ct > rt || io.route[bh]) return;
-  const int ty = tid & 15, tx = tid >> 4;
+  __shared__ __align__(16) float Qs[kPsKc * kPsLd];
+  __shared__ __align__(16) float Ks[kPsKc * kPsLd];
+  // tile t of the lower triangle (row tile rt, column tile ct <= rt, row-major)
+  const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  int rt = (int)((__builtin_sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
+  while (rt * (rt + 1) / 2 > t) --rt;
+  const int ct = t - rt * (rt + 1) / 2;
+  if (io.route[bh]) return;
+  // tx: the 8 keys of a thread (consecutive lanes, consecutive keys: each row of the
+  // tile is written as one contiguous 512-byte run by 16 lanes); ty: its 8 rows
+  const int tx = tid & 15, ty = tid >> 4;
   const int b = bh / dm.hq;
   const int kvh = b * dm.hkv + (bh % dm.hq) / dm.group;
-  const float* qs = qbar + (size_t)bh * dm.nb * D;
-  const float* ks = kbar + (size_t)kvh * dm.nb * D;
-  float acc[TM][TM];
+  const float* qs = qbar + ((size_t)bh * dm.nb + (size_t)rt * kPsTile) * D;
+  const float* ks = kbar + ((size_t)kvh * dm.nb + (size_t)ct * kPsTile) * D;
+  const int qrows = min(kPsTile, dm.nb - rt * kPsTile), krows = min(kPsTile, dm.nb - ct * kPsTile);
+  float acc[kPsTm][kPsTm];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < kPsTm; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = 0.0f;
-  for (int dc = 0; dc < D; dc += KC) {
-    for (int e = tid; e < TL * KC; e += kThreads) {
-      const int r = e / KC, kk = e % KC;
-      const int qr = rt * TL + r, kr = ct * TL + r;
-      Qs[kk * LD + r] = qr < dm.nb ? qs[(size_t)qr * D + dc + kk] : 0.0f;
-      Ks[kk * LD + r] = kr < dm.nb ? ks[(size_t)kr * D + dc + kk] : 0.0f;
+    for (int j = 0; j < kPsTm; ++j) acc[i][j] = 0.0f;
+  // a chunk of one operand is 128 rows x 8 pieces of 4 dims: piece g has row g % 128
+  // and dims 4 (g / 128) .. + 3 of the chunk
+  constexpr int kPieces = kPsTile * kPsKc / 4 / kThreads;  // 4 per thread and operand
+  float4 qv[kPieces], kv[kPieces];
+  auto fetch = [&](int dc) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int g = tid + kThreads * i, r = g % kPsTile, d4 = (g / kPsTile) * 4;
+      qv[i] = r < qrows ? *reinterpret_cast<const float4*>(qs + (size_t)r * D + dc + d4) : make_float4(0, 0, 0, 0);
+      kv[i] = r < krows ? *reinterpret_cast<const float4*>(ks + (size_t)r * D + dc + d4) : make_float4(0, 0, 0, 0);
+    }
+  };
+  fetch(0);
+  for (int dc = 0; dc < D; dc += kPsKc) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int g = tid + kThreads * i, r = g % kPsTile, d4 = (g / kPsTile) * 4;
+      Qs[(d4 + 0) * kPsLd + r] = qv[i].x;
+      Qs[(d4 + 1) * kPsLd + r] = qv[i].y;
+      Qs[(d4 + 2) * kPsLd + r] = qv[i].z;
+      Qs[(d4 + 3) * kPsLd + r] = qv[i].w;
+      Ks[(d4 + 0) * kPsLd + r] = kv[i].x;
+      Ks[(d4 + 1) * kPsLd + r] = kv[i].y;
+      Ks[(d4 + 2) * kPsLd + r] = kv[i].z;
+      Ks[(d4 + 3) * kPsLd + r] = kv[i].w;
     }
     __syncthreads();
+    if (dc + kPsKc < D) fetch(dc + kPsKc);
 #pragma unroll 4
-    for (int kk = 0; kk < KC; ++kk) {
-      const float4 va = *reinterpret_cast<const float4*>(&Qs[kk * LD + ty * TM]);
-      const float4 vb = *reinterpret_cast<const float4*>(&Ks[kk * LD + tx * TM]);
-      const float a[4] = {va.x, va.y, va.z, va.w};
-      const float bb[4] = {vb.x, vb.y, vb.z, vb.w};
+    for (int kk = 0; kk < kPsKc; ++kk) {
+      float a[kPsTm], bb[kPsTm];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < kPsTm; i += 4) {
+        const float4 va = *reinterpret_cast<const float4*>(&Qs[kk * kPsLd + ty * kPsTm + i]);
+        const float4 vb = *reinterpret_cast<const float4*>(&Ks[kk * kPsLd + tx * kPsTm + i]);
+        a[i] = va.x, a[i + 1] = va.y, a[i + 2] = va.z, a[i + 3] = va.w;
+        bb[i] = vb.x, bb[i + 1] = vb.y, bb[i + 2] = vb.z, bb[i + 3] = vb.w;
+      }
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
+      for (int i = 0; i < kPsTm; ++i)
+#pragma unroll
+        for (int j = 0; j < kPsTm; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
     }
     __syncthreads();
   }
   const float c = (float)(1.0 / __builtin_sqrt((double)D));
+  const int kb0 = ct * kPsTile + tx * kPsTm;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int qb = rt * TL + ty * TM + i;
+  for (int i = 0; i < kPsTm; ++i) {
+    const int qb = rt * kPsTile + ty * kPsTm + i;
     if (qb >= dm.nb) continue;
+    float* dst = zbar + ((size_t)bh * dm.nb + qb) * dm.nb + kb0;
+    float z[kPsTm];
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int kb = ct * TL + tx * TM + j;
-      if (kb <= qb) zbar[((size_t)bh * dm.nb + qb) * dm.nb + kb] = acc[i][j] * c;
+    for (int j = 0; j < kPsTm; ++j) z[j] = acc[i][j] * c;
+    if (kb0 + kPsTm - 1 <= qb && ((uintptr_t)dst & 15) == 0) {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(z[0], z[1], z[2], z[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(z[4], z[5], z[6], z[7]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPsTm; ++j)
+        if (kb0 + j <= qb) dst[j] = z[j];
     }
   }
 }
@@ -262,6 +309,11 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   }
   return v;
 }
+// The passes over a row read kRowUnroll chunks of 64 entries before using any of
+// them, so a wave keeps that many loads in flight (one chunk at a time left the
+// kernel waiting on memory latency, not bandwidth).
+constexpr int kRowUnroll = 8;
+
 __global__ __launch_bounds__(kThreads) void pe_rowsoft_kernel(Dims dm, IndexOut io,
                                                               const float* __restrict__ zbar,
                                                               long long* __restrict__ abar,
@@ -270,19 +322,51 @@ __global__ __launch_bounds__(kThreads) void pe_rowsoft_kernel(Dims dm, IndexOut 
   const int qb = dm.nb - 1 - (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6));
   if (qb < 0 || io.route[bh]) return;
   const float* z = zbar + ((size_t)bh * dm.nb + qb) * dm.nb;
+  constexpr int kStep = 64 * kRowUnroll;
   float m = -__builtin_inff();
-  for (int kb = lane; kb <= qb; kb += 64) m = z[kb] > m ? z[kb] : m;
+  for (int base = 0; base <= qb; base += kStep) {
+    float zz[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int kb = base + 64 * u + lane;
+      zz[u] = kb <= qb ? z[kb] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) m = zz[u] > m ? zz[u] : m;
+  }
   m = wave_max_f32(m);
   long long L = 0;
-  for (int kb = lane; kb <= qb; kb += 64) L += fix_rne(exp_crisp(z[kb] - m));
+  for (int base = 0; base <= qb; base += kStep) {
+    float zz[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int kb = base + 64 * u + lane;
+      zz[u] = kb <= qb ? z[kb] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+      if (base + 64 * u + lane <= qb) L += fix_rne(exp_crisp(zz[u] - m));
+  }
   L = wave_sum_i64(L);
   const float l = fix_to_float(L);
   long long* out = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
   long long tot = 0;
-  for (int kb = lane; kb <= qb; kb += 64) {
-    const long long aq = fix_rne(exp_crisp(z[kb] - m) / l);
-    out[kb] = aq;
-    tot += aq;
+  for (int base = 0; base <= qb; base += kStep) {
+    float zz[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int kb = base + 64 * u + lane;
+      zz[u] = kb <= qb ? z[kb] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int kb = base + 64 * u + lane;
+      if (kb <= qb) {
+        const long long aq = fix_rne(exp_crisp(zz[u] - m) / l);
+        out[kb] = aq;
+        tot += aq;
+      }
+    }
   }
   tot = wave_sum_i64(tot);
   if (lane == 0) rowtot[(size_t)bh * dm.nb + qb] = tot;
@@ -451,9 +535,18 @@ __global__ __launch_bounds__(kThreads) void pe_count_kernel(Dims dm, IndexOut io
   const long long* a = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
   int gt = 0, tie = 0;
   if (vstar >= 0 && vstar != 0x7fffffffffffffffLL)
-    for (int kb = lane; kb <= qb; kb += 64) {
-      gt += a[kb] > vstar;
-      tie += a[kb] == vstar;
+    for (int base = 0; base <= qb; base += 64 * kRowUnroll) {
+      long long v[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int kb = base + 64 * u + lane;
+        v[u] = kb <= qb ? a[kb] : -1;  // -1 is below every value and never equals v*
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        gt += v[u] > vstar;
+        tie += v[u] == vstar;
+      }
     }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -562,18 +655,27 @@ __global__ __launch_bounds__(kThreads) void pe_write_kernel(Dims dm, IndexOut io
   long long tcur = all ? 0 : tiepre[(size_t)bh * dm.nb + qb];
   const unsigned long long below = (1ull << lane) - 1ull;
   int cnt = 0;
-  for (int base = 0; base <= qb; base += 64) {
-    const int kb = base + lane;
-    const bool in = kb <= qb;
-    const long long v = (in && !all) ? a[kb] : 0;
-    const bool tie = in && !all && v == vstar;
-    const unsigned long long tmask = __ballot(tie);
-    const int tpos = __popcll(tmask & below);
-    const bool flag = in && (all || v > vstar || kb == qb || (tie && tcur + tpos < rties));
-    tcur += __popcll(tmask);
-    const unsigned long long fmask = __ballot(flag);
-    if (flag) out[cnt + __popcll(fmask & below)] = kb;
-    cnt += __popcll(fmask);
+  for (int base0 = 0; base0 <= qb; base0 += 64 * kRowUnroll) {
+    long long vv[kRowUnroll];  // the loads of kRowUnroll chunks first, then the chunks in order
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int kb = base0 + 64 * u + lane;
+      vv[u] = (kb <= qb && !all) ? a[kb] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int kb = base0 + 64 * u + lane;
+      const bool in = kb <= qb;
+      const long long v = vv[u];
+      const bool tie = in && !all && v == vstar;
+      const unsigned long long tmask = __ballot(tie);
+      const int tpos = __popcll(tmask & below);
+      const bool flag = in && (all || v > vstar || kb == qb || (tie && tcur + tpos < rties));
+      tcur += __popcll(tmask);
+      const unsigned long long fmask = __ballot(flag);
+      if (flag) out[cnt + __popcll(fmask & below)] = kb;
+      cnt += __popcll(fmask);
+    }
   }
 }
 template <typename T>
@@ -597,11 +699,11 @@ hipError_t launch_select(const Dims& dm, const SelectArgs& sa, const void* q, co
       launch_pool<bf16_t>(dm, q, k, io, ws.qbar, ws.kbar, st);
     else
       launch_pool<float>(dm, q, k, io, ws.qbar, ws.kbar, st);
-    const int nt = (dm.nb + 63) / 64;
+    const int nt = (dm.nb + kPsTile - 1) / kPsTile, ntri_t = nt * (nt + 1) / 2;
     if (dm.d == 128)
-      pe_scores_kernel<128><<<dim3(nt, nt, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
+      pe_scores_kernel<128><<<dim3(ntri_t, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
     else
-      pe_scores_kernel<64><<<dim3(nt, nt, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
+      pe_scores_kernel<64><<<dim3(ntri_t, dm.bh), kThreads, 0, st>>>(dm, io, ws.qbar, ws.kbar, ws.zbar);
     pe_rowsoft_kernel<<<rows, kThreads, 0, st>>>(dm, io, ws.zbar, ws.abar, ws.rowtot);
   }
   pe_radix_init_kernel<<<dm.bh, kThreads, 0, st>>>(dm, sa, io, ws.rowtot, ws.hist, ws.state);
