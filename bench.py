@@ -553,6 +553,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K speedup side measurement")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="no amd-smi clock / power samples (off by itself under rocprofv3, whose preloaded "
+                         "library would initialise the GPU in the sampling shell's children)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the compact noise-floor / cumulative / alpha / gamma comparison at 128K and 512K")
     ap.add_argument("--selection-sweep", action="store_true",
@@ -573,12 +576,14 @@ def main():
         return
     import synth
     wl = synth.WORKLOADS[args.config]
-    sampler = ClockSampler()  # before the first GPU call of this process
+    under_profiler = any(k.startswith("ROCPROF") for k in os.environ)
+    sampler = None if args.no_clock or under_profiler else ClockSampler()  # before the first GPU call
     torch.cuda.set_device(0)
     try:
         r = measure(wl, args.steps, args.warmup, with_dense=not args.no_dense, sampler=sampler)
     finally:
-        sampler.stop()
+        if sampler is not None:
+            sampler.stop()
     st = r["stage_ms"]
     total_ms = st["route"] + st["select"] + st["attention"]
     tiles = sum(r["tiles"])
