@@ -440,17 +440,18 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
           }
         };
         // probabilities 2^(s - m_run) of quarter a as packed bf16 and their sum
-        // (from the same bf16 values)
+        // (from the same bf16 values, in two interleaved partial sums so that the
+        // dot instructions do not form one dependent chain)
         auto soft_exp = [&](int a, float m_use) -> float {
-          float qsum = 0.0f;
+          float qs[2] = {0.0f, 0.0f};
 #pragma unroll
           for (int x = 0; x < 16; x += 2) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
             P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
-            qsum = sum_bf16x2(P[a & 1][x >> 1], qsum);
+            qs[(x >> 1) & 1] = sum_bf16x2(P[a & 1][x >> 1], qs[(x >> 1) & 1]);
           }
-          return qsum;
+          return qs[0] + qs[1];
         };
         // Lazy softmax: the reference m_run moves only when a quarter's probability
         // sum leaves [0, 2^64) (or is not a number: the first quarter, where m_run is
