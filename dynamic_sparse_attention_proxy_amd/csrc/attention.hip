@@ -305,7 +305,33 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
     const int item = g * pairs + w;
     const int ntile = kDense ? qb + 1 : ucnt[(size_t)item * dm.nb + qb];
     const int* tl = kDense ? nullptr : ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
-    auto entry = [&](int t) -> int { return kDense ? (t | (kModeFull << 24) | (kModeFull << 26)) : tl[t]; };
+    // Sparse lists are read 64 entries at a time into a register (lane i holds entry
+    // 64 c + i) and taken out with readlane: no scalar load, whose latency the wave
+    // would wait out after every barrier.  The chunk after the current one is loaded
+    // when the current one is entered, 64 tiles before it is needed.
+    int chunk_cur = 0, chunk_nxt = 0;
+    auto load_chunk = [&](int c) -> int {
+      const int i = 64 * c + lane;
+      return i < ntile ? tl[i] : 0;
+    };
+    if (!kDense) {
+      chunk_cur = load_chunk(0);
+      chunk_nxt = load_chunk(1);
+    }
+    auto entry = [&](int t) -> int {
+      if constexpr (kDense) return t | (kModeFull << 24) | (kModeFull << 26);
+      else return __builtin_amdgcn_readlane(chunk_cur, t & 63);
+    };
+    // called once per tile with the next tile's index, after the barrier (every
+    // earlier load of this wave has completed there)
+    auto advance = [&](int t) {
+      if constexpr (!kDense) {
+        if ((t & 63) == 0 && t > 0) {
+          chunk_cur = chunk_nxt;
+          chunk_nxt = load_chunk((t >> 6) + 1);
+        }
+      }
+    };
 
     // K tile -> buffer KI, V^T tile -> buffer 2 + KI (KI a compile-time 0 / 1)
     auto load_tile = [&](int kb, auto KI) {
@@ -336,15 +362,21 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
       dma16<kV + 3 * 1024>(vtile, dv[3], lds_wave);
     };
 
+    int e_next = 0;  // the entry of the tile the next step computes
+
     // One tile: wait for its loads (issued one tile earlier), start the loads of
     // the next tile into the other buffer, compute.  Called with the buffers as
     // constants so every LDS address is a per-lane base plus an immediate.
     auto tile_step = [&](int t, auto KI) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of tile t has landed in LDS
       __builtin_amdgcn_s_barrier();         // every wave's share too; all waves are done with tile t - 1
-      if (t + 1 < ntile) load_tile(entry(t + 1) & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
+      const int e = e_next;
+      if (t + 1 < ntile) {
+        advance(t + 1);
+        e_next = entry(t + 1);
+        load_tile(e_next & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
+      }
       constexpr int kbo = decltype(KI)::value * kTileBytes / 16, vbo = kbo;
-      const int e = entry(t);
       const int kb = e & 0xffffff;
       const int mode = slot_on ? (e >> (24 + 2 * slot)) & 3 : 0;
       if (mode) {
@@ -516,7 +548,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
       }
     };
 
-    if (ntile > 0) load_tile(entry(0) & 0xffffff, std::integral_constant<int, 0>());
+    e_next = ntile > 0 ? entry(0) : 0;
+    if (ntile > 0) load_tile(e_next & 0xffffff, std::integral_constant<int, 0>());
     for (int t = 0; t < ntile; t += 2) {
       tile_step(t, std::integral_constant<int, 0>());
       if (t + 1 < ntile) tile_step(t + 1, std::integral_constant<int, 1>());
