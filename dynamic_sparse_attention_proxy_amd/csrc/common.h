@@ -124,16 +124,30 @@ __device__ __forceinline__ float ordered_to_float(int o) {
   return __int_as_float(o ^ ((o >> 31) & 0x7fffffff));
 }
 
-__device__ __forceinline__ long long shfl_xor_i64(long long v, int m) {
-  int lo = __shfl_xor((int)(v & 0xffffffff), m);
-  int hi = __shfl_xor((int)(v >> 32), m);
+// A 64-bit value moved across lanes by one DPP pattern (both halves with the same
+// control; lanes the pattern or the row mask does not feed read 0).
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ long long dpp_i64(long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(v & 0xffffffff), kCtrl, kRowMask, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), kCtrl, kRowMask, 0xf, true);
   return ((long long)hi << 32) | (unsigned int)lo;
 }
 
+// Sum over the 64 lanes of a wave (all lanes active), returned in every lane.
+// Integer addition is exact, so the order is free: DPP row shifts by 1, 2, 4, 8
+// leave each 16-lane row's sum in its lane 15; row broadcast 15 adds row 0 into
+// row 1 and row 2 into row 3, row broadcast 31 adds lane 31 into rows 2 and 3;
+// lane 63 then holds the total, which readlane hands to the whole wave.
 __device__ __forceinline__ long long wave_sum_i64(long long v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_i64(v, m);
-  return v;
+  v += dpp_i64<0x111>(v);        // row_shr:1
+  v += dpp_i64<0x112>(v);        // row_shr:2
+  v += dpp_i64<0x114>(v);        // row_shr:4
+  v += dpp_i64<0x118>(v);        // row_shr:8
+  v += dpp_i64<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_i64<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffff), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
+  return ((long long)hi << 32) | (unsigned int)lo;
 }
 
 // Sum / max over one workgroup (every thread gets the result); red holds one
