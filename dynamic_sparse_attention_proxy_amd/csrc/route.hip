@@ -245,11 +245,12 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
   const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int rg = tid % Lay::RG, cp = tid / Lay::RG;
   const long long tile_off = ((long long)bh * dm.nb + kb) * (long long)(B * B);
-  float m[4], l[4];
+  float m[4], l[4], rl[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     m[e] = ordered_to_float(m_enc[bh * B + rg * 4 + e]);
     l[e] = fix_to_float(L[bh * B + rg * 4 + e]);
+    rl[e] = 1.0f / l[e];
   }
   long long lo = 0, up = 0, an = 0;
   const bool plain = kb < dm.nb - 1 && dm.qrows == B && kb * B >= ra.w_sink &&
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
       const float z[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double aq = (double)fix_rne_f(exp_crisp(z[e] - m[e]) / l[e]);
+        const double aq = (double)fix_rne_f(quot_rn(exp_crisp(z[e] - m[e]), l[e], rl[e]));
         alld += aq;
         lod += rg * 4 + e >= c ? aq : 0.0;
       }
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void proxy_mass_kernel(Dims dm, RouteArgs
       const int ii = dm.q0 + r;
       if (r < dm.qrows && jj <= ii) {
         const float ev = exp_crisp(z[e] - m[e]);
-        const long long aq = fix_rne(ev / l[e]);
+        const long long aq = fix_rne(quot_rn(ev, l[e], rl[e]));
         // slash block (i - j) / B is (nb - 1 - kb) when r >= c, one less when r < c
         if (r >= c)
           lo += aq;

@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void pe_rowsoft_kernel(Dims dm, IndexOut 
       if (base + 64 * u + lane <= qb) L += fix_rne(exp_crisp(zz[u] - m));
   }
   L = wave_sum_i64(L);
-  const float l = fix_to_float(L);
+  const float l = fix_to_float(L), rl = 1.0f / l;
   long long* out = abar + (size_t)bh * dm.ntri + (size_t)qb * (qb + 1) / 2;
   long long tot = 0;
   for (int base = 0; base <= qb; base += kStep) {
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void pe_rowsoft_kernel(Dims dm, IndexOut 
     for (int u = 0; u < kRowUnroll; ++u) {
       const int kb = base + 64 * u + lane;
       if (kb <= qb) {
-        const long long aq = fix_rne(exp_crisp(zz[u] - m) / l);
+        const long long aq = fix_rne(quot_rn(exp_crisp(zz[u] - m), l, rl));
         out[kb] = aq;
         tot += aq;
       }
