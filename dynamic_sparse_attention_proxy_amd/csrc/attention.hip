@@ -364,18 +364,27 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
 
     int e_next = 0;  // the entry of the tile the next step computes
 
-    // One tile: wait for its loads (issued one tile earlier), start the loads of
-    // the next tile into the other buffer, compute.  Called with the buffers as
-    // constants so every LDS address is a per-lane base plus an immediate.
+    // One tile: wait for its loads (issued during the previous tile), compute it,
+    // and start the loads of the next tile into the other buffer on the way.  Called
+    // with the buffers as constants so every LDS address is a per-lane base plus an
+    // immediate.
     auto tile_step = [&](int t, auto KI) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of tile t has landed in LDS
       __builtin_amdgcn_s_barrier();         // every wave's share too; all waves are done with tile t - 1
       const int e = e_next;
+      int e_dma = -1;
       if (t + 1 < ntile) {
         advance(t + 1);
         e_next = entry(t + 1);
-        load_tile(e_next & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
+        e_dma = e_next;
       }
+      // the next tile's direct loads into the other buffer (free since the barrier);
+      // issued in the second quarter step rather than right after the barrier: 0.9 %
+      // faster on the sparse launch (same bits), the loads still land long before
+      // the next tile
+      auto issue_next = [&]() {
+        if (e_dma >= 0) load_tile(e_dma & 0xffffff, std::integral_constant<int, 1 - decltype(KI)::value>());
+      };
       constexpr int kbo = decltype(KI)::value * kTileBytes / 16, vbo = kbo;
       const int kb = e & 0xffffff;
       const int mode = slot_on ? (e >> (24 + 2 * slot)) & 3 : 0;
@@ -539,12 +548,15 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
           __builtin_amdgcn_iglp_opt(0);
           if (a < 3) qk(a + 1);
           if (a < 2) kload(a + 2);
+          if (a == 1) issue_next();
           if (a > 0) { pinf(vf); pv(a - 1); }
           soft(a);
         }
         vload(3);
         pinf(vf);
         pv(3);
+      } else {
+        issue_next();
       }
     };
 
