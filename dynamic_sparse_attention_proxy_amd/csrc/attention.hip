@@ -143,10 +143,13 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // lds_wave + kBufImm addresses the slot: lds_wave is a per-wave scalar, the
 // constant part is encoded in the instruction stream.  The LDS destination goes
 // through m0; nothing else in these kernels uses m0 (checked in the generated
-// code), so the compiler's treatment of m0 as reserved does not matter here.
+// code), so the compiler's treatment of m0 as reserved does not matter here.  A
+// scalar write of m0 needs one wait state before an LDS DMA reads it (the
+// compiler keeps that distance for its own DMA instructions but cannot see inside
+// an asm block), hence the s_nop.
 template <unsigned kLdsConst>
 __device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, unsigned lds_wave) {
-  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(base), "s"(lds_wave), "n"(kLdsConst)
                : "memory", "m0");
@@ -154,7 +157,7 @@ __device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, 
 // the same with a per-lane 64-bit address
 template <unsigned kLdsConst>
 __device__ __forceinline__ void dma16_lane(const unsigned char* addr, unsigned lds_wave) {
-  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(addr), "s"(lds_wave), "n"(kLdsConst)
                : "memory", "m0");
