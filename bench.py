@@ -420,12 +420,13 @@ def measure(wl, steps, warmup, with_dense=True, dense_reps=None, sampler=None):
         ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock = sampler.window(wall0, time.time()) if sampler is not None else None
+    wall1 = time.time()
+    clock = sampler.window(wall0, wall1) if sampler is not None else None
     for i in range(steps):
         stage["route"].append(ev[i][0].elapsed_time(ev[i][1]))
         stage["select"].append(ev[i][1].elapsed_time(ev[i][2]))
         stage["attention"].append(ev[i][2].elapsed_time(ev[i][3]))
-    res = {"I": I, "spec": spec, "bufs": bufs, "wall_s": wall, "clock": clock,
+    res = {"I": I, "spec": spec, "bufs": bufs, "wall_s": wall, "clock": clock, "timed_window": (wall0, wall1),
            "stage_bytes": stage_bytes(wl, bufs),
            "stage_ms": {kk: sum(vv) / len(vv) for kk, vv in stage.items()}}
     if with_dense:
@@ -553,6 +554,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K speedup side measurement")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--clock-log", default=None,
+                    help="also write the raw amd-smi samples (each after an '@@ <unix time>' line) and the timed "
+                         "window of the sparse steps to this path")
     ap.add_argument("--no-clock", action="store_true",
                     help="no amd-smi clock / power samples (off by itself under rocprofv3, whose preloaded "
                          "library would initialise the GPU in the sampling shell's children)")
@@ -584,6 +588,10 @@ def main():
     finally:
         if sampler is not None:
             sampler.stop()
+    if args.clock_log and sampler is not None and os.path.exists(sampler.path):
+        with open(sampler.path) as f_in, open(args.clock_log, "w") as f_out:
+            f_out.write(f"# timed window of the sparse steps: {r['timed_window'][0]:.3f} {r['timed_window'][1]:.3f}\n")
+            f_out.write(f_in.read())
     st = r["stage_ms"]
     total_ms = st["route"] + st["select"] + st["attention"]
     tiles = sum(r["tiles"])
