@@ -401,7 +401,10 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
         }
         const bool masked = diag || mode != kModeFull || (kb + 1) * B > dm.n;
         const bool slow = masked || tile_bias;
-        const float ksc = slow ? 1.0f : sl2;  // multiplier from stored scores to log2 units
+        // multiplier from stored scores to log2 units, tile-uniform: kept in a scalar
+        // register so the score FMA reads it directly
+        const float ksc = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, slow ? 1.0f : sl2)));
 
         f32x16 S[2];       // scores of quarters a and a + 1 (by parity)
         unsigned P[2][8];  // packed bf16 probabilities of quarters a - 1 and a (by parity), [4 s2 + j]
@@ -463,22 +466,23 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
               }
             }
             if (masked) {
-              // the kept keys of a row form one range: C <= rr (lower part) and / or
-              // C > rr (upper part), and C < nl (inside the sequence); an empty range
-              // is moved past every C
+              // the kept keys of a row form one range lo <= C <= hi: C <= rr (lower
+              // part) and / or C > rr (upper part), and C < nl (inside the sequence)
               const bool lower_ok = (mode & kModeLower) != 0;
               const bool upper_ok = (mode & kModeUpper) != 0 && !diag;
               const int nl = dm.n - kb * B - 8 * hl;
-              int lo = lower_ok ? 0 : rr + 1;
-              int hi = upper_ok ? nl - 1 : min(rr, nl - 1);
-              if (hi < lo) lo = 1 << 20, hi = lo;
-              const unsigned span = (unsigned)(hi - lo);
-              int nlo = -lo;
-              asm volatile("" : "+v"(nlo));
+              const int lo = lower_ok ? 0 : rr + 1;
+              const int hi = upper_ok ? nl - 1 : min(rr, nl - 1);
+              // kept columns of this quarter as a bit mask over C - 32 a (bits lo .. hi;
+              // 0 when the range is empty or misses the quarter), then one signed bit
+              // extract (0 or all ones) and one bit select per score
+              const int lj = min(max(lo - 32 * a, 0), 32), hj = min(max(hi - 32 * a, -1), 31);
+              const unsigned keep = (lj < 32 ? ~0u << lj : 0u) & (hj >= 0 ? ~0u >> (31 - hj) : 0u);
+              const unsigned ninf = __float_as_uint(-__builtin_inff());
 #pragma unroll
               for (int x = 0; x < 16; ++x) {
-                const int C = 32 * a + 16 * (x >> 3) + (x & 7);
-                if ((unsigned)(C + nlo) > span) s[x] = -__builtin_inff();
+                const unsigned sel = (unsigned)__builtin_amdgcn_sbfe((int)keep, 16 * (x >> 3) + (x & 7), 1);
+                s[x] = __uint_as_float((sel & __float_as_uint(s[x])) | (~sel & ninf));
               }
             }
           }
@@ -629,10 +633,12 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* __restri
 // time, from the heads' index sets, then compacts them in order.
 __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, IndexOut io, int* __restrict__ ulist,
                                                          int* __restrict__ ucnt) {
-  constexpr int kChunk = 4096;
-  __shared__ unsigned int modes[kChunk / 4];  // one byte per key block: bits 0-1 first head, 2-3 second
-  __shared__ int wave_cnt[4];
-  const int qb = blockIdx.x, item = blockIdx.y, tid = threadIdx.x;
+  constexpr int kChunk = 4096;  // 256 threads x 16 key blocks
+  // one byte per key block: bits 0-1 first head, 2-3 second
+  __shared__ __align__(16) unsigned int modes[kChunk / 4];
+  __shared__ int stage[kChunk];  // one chunk's entries in order, then copied out
+  __shared__ int wave_tot[4];
+  const int qb = blockIdx.x, item = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = item / pairs, w = item % pairs;
   const int bidx = g / dm.hkv, gh = g % dm.hkv;
   int* out = ulist + (size_t)item * dm.ntri + (size_t)qb * (qb + 1) / 2;
@@ -669,15 +675,41 @@ __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, Ind
       }
     }
     __syncthreads();
-    for (int base = c0; base < c1; base += 256) {
-      const int kb = base + tid;
-      const unsigned m = kb < c1 ? (modes[(kb - c0) >> 2] >> (8 * ((kb - c0) & 3))) & 15u : 0u;
-      int tot;
-      const int pos = block_compact(m != 0, wave_cnt, &tot);
-      if (m) out[cnt + pos] = kb | (int)((m & 3u) << 24) | (int)((m >> 2) << 26);
-      cnt += tot;
+    // thread tid compacts key blocks c0 + 16 tid .. + 15 (four words; blocks at or past
+    // c1 were never marked): one block-wide prefix of the per-thread counts, the
+    // entries staged in LDS in ascending order, then one coalesced copy
+    const uint4 mw = reinterpret_cast<const uint4*>(modes)[tid];
+    const unsigned wd[4] = {mw.x, mw.y, mw.z, mw.w};
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsigned nz = wd[j] | (wd[j] >> 1);
+      nz |= nz >> 2;
+      n += __popc(nz & 0x01010101u);
+    }
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int pos = incl - n, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      if (w2 < wave) pos += wave_tot[w2];
+      tot += wave_tot[w2];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const unsigned m = (wd[j >> 2] >> (8 * (j & 3))) & 15u;
+      if (m) stage[pos++] = (c0 + 16 * tid + j) | (int)((m & 3u) << 24) | (int)((m >> 2) << 26);
     }
     __syncthreads();
+    for (int i = tid; i < tot; i += 256) out[cnt + i] = stage[i];
+    cnt += tot;
+    __syncthreads();  // modes, stage and wave_tot are reused by the next chunk
   }
   if (tid == 0) ucnt[(size_t)item * dm.nb + qb] = cnt;
 }
