@@ -657,21 +657,39 @@ __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, Ind
           if (mode) atomicOr(&modes[(kb - c0) >> 2], (unsigned)mode << (8 * ((kb - c0) & 3) + 2 * s2));
         }
       };
-      if (io.route[bh]) {
-        // vertical block kb: whole tile; slash block s: lower triangle of tile qb - s
-        // and upper triangle of tile qb - s - 1
-        const int nv = io.vs_count[bh * 2], ns = io.vs_count[bh * 2 + 1];
-        const int* V = io.vs_vertical + (size_t)bh * dm.nb;
-        const int* S = io.vs_slash + (size_t)bh * dm.nb;
-        for (int i = tid; i < nv; i += 256) mark(V[i], kModeFull);
-        for (int i = tid; i < ns; i += 256) {
-          mark(qb - S[i], kModeLower);
-          mark(qb - S[i] - 1, kModeUpper);
+      // the head's list extents, all read at once (the route picks which apply), then
+      // each list read eight entries per thread ahead of their marks, so a thread waits
+      // on one round of loads per 2048 entries instead of one per 256
+      const bool vs = io.route[bh] != 0;
+      const int nv = io.vs_count[bh * 2], ns = io.vs_count[bh * 2 + 1];
+      const int* rp = io.pe_rowptr + (size_t)bh * (dm.nb + 1);
+      const int p0 = rp[qb], p1 = rp[qb + 1];
+      auto mark_list = [&](const int* src, int count, bool slash) {
+        for (int base = 0; base < count; base += 8 * 256) {
+          int e[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = base + 256 * u + tid;
+            e[u] = i < count ? src[i] : -1;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (e[u] < 0) continue;
+            if (slash) {
+              // slash block s: lower triangle of tile qb - s, upper triangle of tile qb - s - 1
+              mark(qb - e[u], kModeLower);
+              mark(qb - e[u] - 1, kModeUpper);
+            } else {
+              mark(e[u], kModeFull);  // vertical block or PE key block: whole tile
+            }
+          }
         }
+      };
+      if (vs) {
+        mark_list(io.vs_vertical + (size_t)bh * dm.nb, nv, false);
+        mark_list(io.vs_slash + (size_t)bh * dm.nb, ns, true);
       } else {
-        const int* rp = io.pe_rowptr + (size_t)bh * (dm.nb + 1);
-        const int* col = io.pe_col + (size_t)bh * io.pe_cap;
-        for (int p = rp[qb] + tid; p < rp[qb + 1]; p += 256) mark(col[p], kModeFull);
+        mark_list(io.pe_col + (size_t)bh * io.pe_cap + p0, p1 - p0, false);
       }
     }
     __syncthreads();

@@ -73,40 +73,69 @@ def _check_attention(wl, I, X, spec, bufs, ref, rows, what, heads=None):
     log(what, "max-abs sparse", err_sp, "dense", err_de)
     assert np.isfinite(o_sp).all() and np.isfinite(o_de).all()
     if wl.dtype == "f32" and wl.qk_scale > 1.0:
-        tol = _peaked_f32_tolerance(wl, I, rows, hs)[:, :, None]
-        log(what, "row tolerance", float(tol.min()), float(tol.max()))
-        assert np.all(np.abs(o_sp - r_sp) <= tol), f"sparse max-abs {err_sp}"
-        assert np.all(np.abs(o_de - r_de) <= tol), f"dense max-abs {err_de}"
+        for got, want, sp, kind in ((o_sp, r_sp, specs, "sparse"), (o_de, r_de, [dict(kind="dense")] * len(specs),
+                                                                      "dense")):
+            tol = _peaked_f32_tolerance(wl, I, rows, hs, sp)
+            err = np.abs(got - want)
+            log(what, kind, "tolerance min / median / max", float(tol.min()), float(np.median(tol)), float(tol.max()),
+                "max err/tol", float((err / tol).max()))
+            assert np.all(err <= tol), f"{kind}: worst {np.unravel_index(np.argmax(err / tol), err.shape)}"
         return
     assert err_sp <= TOL[wl.dtype], f"sparse max-abs {err_sp}"
     assert err_de <= TOL[wl.dtype], f"dense max-abs {err_de}"
 
 
-def _peaked_f32_tolerance(wl, I, rows, heads):
-    """Per-row fp32 bar for inputs with logits of thousands of nats.
+def _peaked_f32_tolerance(wl, I, rows, heads, specs):
+    """Per-element fp32 bar [heads, rows, d] for inputs with logits of thousands of nats.
 
-    An fp32 logit s = fl(q . k) c + bias carries an absolute rounding error up to
-    E = gamma_(d+2) (c sum_t |q_t k_t| + |bias|), gamma_m = m u / (1 - m u),
-    u = 2^-24: proportional to the logit's size, not bounded by the 1e-5 bar.  A
-    softmax-weighted mean moves by at most 2 max_j |ds_j| max_j |v_j| under
-    logit perturbations ds, so each row is held to 1e-5 (the rounding of the
-    probabilities and of the weighted sum, as for every other fp32 case) plus
-    that first-order term with the row's largest E over its causal keys.
+    An fp32 logit s_j = fl(q . k_j) c + bias carries an absolute rounding error up to
+    E_j = gamma_(d+2) (c sum_t |q_t k_jt| + |bias_j|), gamma_m = m u / (1 - m u),
+    u = 2^-24: proportional to the logit's size, not bounded by the 1e-5 bar.  To
+    first order in the logit errors ds_j (|ds_j| <= E_j), the softmax-weighted mean
+    o = sum_j p_j v_j moves by sum_j p_j (ds_j - sum_k p_k ds_k) v_j
+    = sum_j p_j (ds_j - sum_k p_k ds_k) (v_j - o), since the weights' changes sum to
+    zero.  So |do_t| <= sum_j p_j (E_j + Ebar) |v_jt - o_t| with Ebar = sum_k p_k E_k,
+    evaluated with the fp64 probabilities of the row's kept keys (the index set's
+    mask).  Each element is held to 1e-5 (the rounding of the probabilities and of the
+    weighted sum, as for every other fp32 case) plus twice that first-order term (the
+    factor covers the second-order terms: E_j is below 0.02 nats here).  On rows that
+    one key dominates the term vanishes (o is that key's value), so the bar is close to
+    1e-5 there and the check sees small errors; it grows only where several keys with
+    logits of thousands of nats compete.
     """
+    import torch
     n, d = wl.n, wl.d
     rows = np.arange(n) if rows is None else np.asarray(rows)
     G = wl.hq // wl.hkv
     u = 2.0 ** -24
     gam = (d + 2) * u / (1 - (d + 2) * u)
     c = 1.0 / np.sqrt(d)
-    out = np.empty((len(heads), len(rows)))
-    causal = np.arange(n)[None, :] <= rows[:, None]
+    nb = oracle.num_blocks(n, wl.block)
+    r_t = torch.as_tensor(rows, dtype=torch.long)
+    j = torch.arange(n)
+    out = np.empty((len(heads), len(rows), d))
     for hi, h in enumerate(heads):
         g = h // G
-        mag = c * (np.abs(I.q[h][rows].astype(np.float64)) @ np.abs(I.k[g].astype(np.float64)).T)
-        bmax = float(np.abs(I.bias_values[h]).max()) if I.bias_values.size else 0.0
-        E = gam * (np.where(causal, mag, 0.0).max(axis=1) + bmax)
-        out[hi] = TOL["f32"] + 2.0 * E * float(np.abs(I.v[g]).max())
+        Q = torch.from_numpy(I.q[h][rows]).double()
+        K = torch.from_numpy(I.k[g]).double()
+        V = torch.from_numpy(I.v[g]).double()
+        S = (Q @ K.T) * c
+        Bv = torch.zeros_like(S)
+        if I.bias_offsets.size:
+            for off, val in zip(I.bias_offsets[h], I.bias_values[h]):
+                if val != 0 and off >= 0:
+                    jj = r_t - int(off)
+                    ok = jj >= 0
+                    Bv[torch.nonzero(ok).ravel(), jj[ok]] += float(val)
+        mask = oracle._allowed(specs[h], r_t, j, wl.block, nb)
+        P = torch.softmax((S + Bv).masked_fill(~mask, float("-inf")), dim=1)
+        O = P @ V
+        E = gam * (c * (Q.abs() @ K.abs().T) + Bv.abs()) * mask
+        W = P * (E + (P * E).sum(dim=1, keepdim=True))
+        for r0 in range(0, len(rows), 64):
+            sl = slice(r0, r0 + 64)
+            first = (W[sl, :, None] * (V[None] - O[sl, None, :]).abs()).sum(dim=1)
+            out[hi, sl] = TOL["f32"] + 2.0 * first.numpy()
     return out
 
 
