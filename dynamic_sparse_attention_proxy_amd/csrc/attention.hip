@@ -446,8 +446,7 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
               oacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[4 * s2 + t2]), Pb, oacc[t2], 0, 0, 0);
           }
         };
-        // masks / bias and the running max of quarter a; rescales O and l when needed
-        // masks and bias of quarter a (tiles that need them only)
+        // masks and bias of quarter a (tiles that need them only), in log2 units
         auto soft_mask = [&](int a) {
           f32x16& s = S[a & 1];
           if (slow) {
