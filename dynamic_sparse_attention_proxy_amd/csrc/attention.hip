@@ -656,9 +656,9 @@ __global__ __launch_bounds__(256) void pair_tiles_kernel(Dims dm, int pairs, Ind
           if (mode) atomicOr(&modes[(kb - c0) >> 2], (unsigned)mode << (8 * ((kb - c0) & 3) + 2 * s2));
         }
       };
-      // the head's list extents, all read at once (the route picks which apply), then
-      // each list read eight entries per thread ahead of their marks, so a thread waits
-      // on one round of loads per 2048 entries instead of one per 256
+      // the route picks the head's lists; each list is read eight entries per thread
+      // ahead of their marks, so a thread waits on one round of loads per 2048 entries
+      // instead of one per 256
       const bool vs = io.route[bh] != 0;
       const int nv = io.vs_count[bh * 2], ns = io.vs_count[bh * 2 + 1];
       const int* rp = io.pe_rowptr + (size_t)bh * (dm.nb + 1);
