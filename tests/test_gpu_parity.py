@@ -301,7 +301,9 @@ def test_cumulative_mode_multichunk_512k():
     compaction over four chunks of 1024 blocks, carrying the tie count across chunks.
     VS lists bit-exact against the oracle's cumulative rule on the oracle's masses
     (which the GPU's equal bit for bit); PE index sets as in the noise-floor mode;
-    attention on the new sets within the bar on 256 sampled rows of eight heads."""
+    the attention step's key-tile lists bit for bit (VS lists of 3500+ blocks, so the
+    slash marking runs over more than one 2048-entry round per query block); attention on
+    the new sets within the bar on 256 sampled rows of eight heads."""
     import dataclasses
     wl, I, X, spec, bufs, ref = _case("llama_512k")
     spec_c = dataclasses.replace(spec, select_mode=crisp.SELECT_CUMULATIVE)
@@ -322,6 +324,10 @@ def test_cumulative_mode_multichunk_512k():
     nv = [len(cum["heads"][h]["vertical"]) for h in range(wl.hq) if pr["route"][h]]
     log("512k cumulative vertical blocks per VS head", nv)
     assert min(nv) > 1024  # the selected lists themselves span several chunks
+    run_sparse(spec_c, X, b2)
+    with Timer("tile lists 512k cumulative"):
+        bad = compare_tile_lists(spec_c, b2, cum)
+    assert not bad, "\n".join(bad[:20])
     heads = [0, 1, 2, 3, 16, 17, 18, 19]
     _check_attention(wl, I, X, spec_c, b2, cum, synth.sample_rows(wl), "512k cumulative", heads=heads)
 
