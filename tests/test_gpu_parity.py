@@ -83,6 +83,69 @@ def _check_attention(wl, I, X, spec, bufs, ref, rows, what, heads=None):
         return
     assert err_sp <= TOL[wl.dtype], f"sparse max-abs {err_sp}"
     assert err_de <= TOL[wl.dtype], f"dense max-abs {err_de}"
+    if wl.dtype == "bf16":
+        for got, want, sp, kind in ((o_sp, r_sp, specs, "sparse"), (o_de, r_de, [dict(kind="dense")] * len(specs),
+                                                                      "dense")):
+            tol = np.minimum(_bf16_tolerance(wl, I, rows, hs, sp), TOL["bf16"])
+            err = np.abs(got - want)
+            log(what, kind, "bf16 bar min / median / max", float(tol.min()), float(np.median(tol)),
+                float(tol.max()), "max err/bar", float((err / tol).max()))
+            assert np.all(err <= tol), f"{kind}: worst {np.unravel_index(np.argmax(err / tol), err.shape)}"
+
+
+def _bf16_tolerance(wl, I, rows, heads, specs):
+    """Per-element bar [heads, rows, d] for the bf16 matrix engine, from its arithmetic.
+
+    The probabilities are rounded to bf16 (unit roundoff 2^-8) before both the P V
+    product and the row sums, so the normalised output moves by
+    sum_j p_j delta_j (v_j - o) / sum_j p_j (1 + delta_j), at most
+    2^-8 E_p|v - o| / (1 - 2^-8) <= 1.004 * 2^-8 (E_p|v| + |o|), and the final
+    conversion of o to bf16 adds at most 2^-8 |o|.  The fp32 accumulations of O and of
+    the row sum take about n_kept / 16 + 32 steps, each rounding within
+    gamma_m (E_p|v| + |o|) overall; a logit carries at most
+    ds = gamma_(d/16+17) c sum_t |q_t k_t| (bf16 products exact in fp32, d/16 matrix
+    steps of 16 products), which moves o by at most 2 max_j ds_j (E_p|v| + |o|) to first
+    order; the exponent's argument and v_exp_f32 add a relative 2^-16 at most.  So
+    |o - o_exact| <= 1.01 (2^-7 + 2^-16 + gamma_m + 2 max_j ds_j) (E_p|v| + |o|) + 1e-5,
+    with the fp64 probabilities of the row's kept keys.  It never exceeds the 2e-2 bar
+    stated for bf16 on these inputs, and it is about 3e-4 for a typical element
+    (2e-2 throughout before)."""
+    import torch
+    n, d = wl.n, wl.d
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    G = wl.hq // wl.hkv
+    u = 2.0 ** -24
+    c = 1.0 / np.sqrt(d)
+    nb = oracle.num_blocks(n, wl.block)
+    r_t = torch.as_tensor(rows, dtype=torch.long)
+    out = np.empty((len(heads), len(rows), d))
+    k_steps = d / 16 + 17
+    gam_s = k_steps * u / (1 - k_steps * u)
+    for hi, h in enumerate(heads):
+        g = h // G
+        K = torch.from_numpy(I.k[g]).double()
+        V = torch.from_numpy(I.v[g]).double()
+        Q = torch.from_numpy(I.q[h][rows]).double()
+        for r0 in range(0, len(rows), 64):
+            rr = r_t[r0:r0 + 64]
+            jmax = int(rr.max()) + 1
+            S = (Q[r0:r0 + 64] @ K[:jmax].T) * c
+            if I.bias_offsets.size:
+                for off, val in zip(I.bias_offsets[h], I.bias_values[h]):
+                    if val != 0 and off >= 0:
+                        jj = rr - int(off)
+                        ok = (jj >= 0) & (jj < jmax)
+                        S[torch.nonzero(ok).ravel(), jj[ok]] += float(val)
+            mask = oracle._allowed(specs[h], rr, torch.arange(jmax), wl.block, nb)
+            P = torch.softmax(S.masked_fill(~mask, float("-inf")), dim=1)
+            O = P @ V[:jmax]
+            Ev = P @ V[:jmax].abs()
+            m = mask.sum(dim=1, keepdim=True).double() / 16 + 32
+            gam = m * u / (1 - m * u)
+            ds = gam_s * ((Q[r0:r0 + 64].abs() @ K[:jmax].abs().T) * c * mask).max(dim=1, keepdim=True).values
+            coef = 1.01 * (2.0 ** -7 + 2.0 ** -16 + gam + 2.0 * ds)
+            out[hi, r0:r0 + 64] = (coef * (Ev + O.abs()) + 1e-5).numpy()
+    return out
 
 
 def _peaked_f32_tolerance(wl, I, rows, heads, specs):
