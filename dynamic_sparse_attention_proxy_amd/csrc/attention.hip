@@ -243,6 +243,8 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
   }
   const unsigned lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * 4096);
   const int xcd = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7;  // hardware XCC id (4 bits)
+  int ones_bits;  // (1, 1) in bf16, in a scalar register for the row-sum dot products
+  asm volatile("s_mov_b32 %0, 0x3f803f80" : "=s"(ones_bits));
   const int combos = dm.bkv * pairs;
 
   for (;;) {
@@ -490,13 +492,22 @@ __global__ __launch_bounds__(512, 1) void attn_mfma_kernel(const bf16_t* __restr
         // (from the same bf16 values, in two interleaved partial sums so that the
         // dot instructions do not form one dependent chain)
         auto soft_exp = [&](int a, float m_use) -> float {
-          float qs[2] = {0.0f, 0.0f};
+          float qs[2];
 #pragma unroll
           for (int x = 0; x < 16; x += 2) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x], ksc, -m_use));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[a & 1][x + 1], ksc, -m_use));
             P[a & 1][x >> 1] = pack_bf16x2(p0, p1);
-            qs[(x >> 1) & 1] = sum_bf16x2(P[a & 1][x >> 1], qs[(x >> 1) & 1]);
+            if (x < 4) {
+              // first term of each partial sum: the three-operand dot with a zero
+              // addend (the two-operand form the compiler picks accumulates in place
+              // and would need the zero moved in first)
+              float r;
+              asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(P[a & 1][x >> 1]), "s"(ones_bits));
+              qs[(x >> 1) & 1] = r;
+            } else {
+              qs[(x >> 1) & 1] = sum_bf16x2(P[a & 1][x >> 1], qs[(x >> 1) & 1]);
+            }
           }
           return qs[0] + qs[1];
         };
