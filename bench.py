@@ -592,6 +592,8 @@ def main():
         with open(sampler.path) as f_in, open(args.clock_log, "w") as f_out:
             f_out.write(f"# timed window of the sparse steps: {r['timed_window'][0]:.3f} {r['timed_window'][1]:.3f}\n")
             f_out.write(f_in.read())
+    if sampler is not None and os.path.exists(sampler.path):
+        os.remove(sampler.path)  # the raw samples are in the bench line (and in --clock-log when asked for)
     st = r["stage_ms"]
     total_ms = st["route"] + st["select"] + st["attention"]
     tiles = sum(r["tiles"])
