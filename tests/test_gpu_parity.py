@@ -395,6 +395,58 @@ def test_cumulative_mode_multichunk_512k():
     _check_attention(wl, I, X, spec_c, b2, cum, synth.sample_rows(wl), "512k cumulative", heads=heads)
 
 
+@pytest.mark.timeout(900)
+def test_caller_supplied_index_sets():
+    """crisp_sparse_prefill on index sets the caller builds (seeded random, within the
+    header's contract: ascending lists of in-range blocks, PE rows that hold their
+    diagonal block, every VS head keeping offset block 0) instead of the ones
+    crisp_select_indices writes: routes drawn per head, VS lists from one block to
+    all of them, PE rows from the diagonal alone to the whole causal row.  The
+    key-tile lists bit for bit, then attention on 256 sampled rows of every head
+    against the oracle on the same sets, to the flat and the per-element bf16 bars."""
+    import torch
+    wl, I, X, spec, _, _ = _case("llama_32k")
+    bufs = crisp.Buffers(spec)  # its own buffers: the cached case keeps the selected sets
+    nb = spec.num_blocks
+    rng = np.random.default_rng(20240611)
+    bh = spec.heads
+    route = rng.integers(0, 2, size=bh).astype(np.uint8)
+    route[:2] = (1, 0)  # both kinds at least once
+    heads = []
+    vs_count = np.zeros((bh, 2), np.int32)
+    vs_vertical = np.zeros((bh, nb), np.int32)
+    vs_slash = np.zeros((bh, nb), np.int32)
+    pe_rowptr = np.zeros((bh, nb + 1), np.int32)
+    pe_col = np.zeros((bh, bufs.pe_cap), np.int32)
+    for h in range(bh):
+        if route[h]:
+            vert = np.sort(rng.choice(nb, size=int(rng.integers(0, nb + 1)), replace=False)).astype(np.int32)
+            sl = np.union1d([0], rng.choice(nb, size=int(rng.integers(0, nb)), replace=False)).astype(np.int32)
+            vs_count[h] = (len(vert), len(sl))
+            vs_vertical[h, : len(vert)] = vert
+            vs_slash[h, : len(sl)] = sl
+            heads.append(dict(route=1, vertical=vert, slash=sl))
+        else:
+            keep_p = rng.uniform(0.0, 1.0)
+            rows = []
+            for qb in range(nb):
+                row = np.flatnonzero(rng.random(qb + 1) < keep_p)
+                rows.append(np.union1d(row, [qb]).astype(np.int32))
+            rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+            cols = np.concatenate(rows).astype(np.int32)
+            pe_rowptr[h] = rp
+            pe_col[h, : len(cols)] = cols
+            heads.append(dict(route=0, rowptr=rp, cols=cols))
+    for name, arr in (("route", route), ("vs_count", vs_count), ("vs_vertical", vs_vertical),
+                      ("vs_slash", vs_slash), ("pe_rowptr", pe_rowptr), ("pe_col", pe_col)):
+        getattr(bufs, name).copy_(torch.from_numpy(arr).to(getattr(bufs, name).device))
+    ref = dict(heads=heads)
+    run_sparse(spec, X, bufs)
+    bad = compare_tile_lists(spec, bufs, ref)
+    assert not bad, "\n".join(bad[:20])
+    _check_attention(wl, I, X, spec, bufs, ref, synth.sample_rows(wl), "caller-supplied index sets")
+
+
 # Every middle block ties (Q = K = 0), and one head carries a 12-nat bias on the main
 # diagonal, enough mass at the anchor positions to route it to VS but not enough to
 # reach gamma = 0.95 alone: the cumulative cut falls inside the run of tied blocks,
