@@ -170,6 +170,12 @@ crisp_status crisp_select_indices(const crisp_shape* shape, const crisp_config* 
  * + bias, times v.  Allowed (i, j), always with j <= i:
  *   VS head: key block j / B in vs_vertical, or offset block (i - j) / B in vs_slash;
  *   PE head: key block j / B listed in the PE row of query block i / B.
+ * idx may come from crisp_select_indices or from the caller; either way its lists
+ * must be ascending with entries in [0, N_b), vs_count at most N_b, pe_rowptr
+ * non-decreasing from 0 with pe_rowptr[N_b] <= pe_cap, and every query row needs at
+ * least one allowed key (the selection always keeps offset block 0 of a VS head and
+ * the diagonal block of every PE row).  These device-side contents are read as
+ * given, not checked.
  * Reads q, k, v, bias, idx; writes o. */
 crisp_status crisp_sparse_prefill(const crisp_shape* shape, const crisp_config* cfg, const void* q,
                                   const void* k, const void* v, const crisp_rel_bias* bias,
