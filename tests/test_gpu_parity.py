@@ -396,16 +396,18 @@ def test_cumulative_mode_multichunk_512k():
 
 
 @pytest.mark.timeout(900)
-def test_caller_supplied_index_sets():
+@pytest.mark.parametrize("name", ["llama_32k", "tiny"])
+def test_caller_supplied_index_sets(name):
     """crisp_sparse_prefill on index sets the caller builds (seeded random, within the
     header's contract: ascending lists of in-range blocks, PE rows that hold their
     diagonal block, every VS head keeping offset block 0) instead of the ones
     crisp_select_indices writes: routes drawn per head, VS lists from one block to
     all of them, PE rows from the diagonal alone to the whole causal row.  The
     key-tile lists bit for bit, then attention on 256 sampled rows of every head
-    against the oracle on the same sets, to the flat and the per-element bf16 bars."""
+    (every row of the tiny fp32 layer, on the vector engine) against the oracle on the
+    same sets, to the flat bar and, in bf16, the per-element bar."""
     import torch
-    wl, I, X, spec, _, _ = _case("llama_32k")
+    wl, I, X, spec, _, _ = _case(name)
     bufs = crisp.Buffers(spec)  # its own buffers: the cached case keeps the selected sets
     nb = spec.num_blocks
     rng = np.random.default_rng(20240611)
@@ -437,14 +439,15 @@ def test_caller_supplied_index_sets():
             pe_rowptr[h] = rp
             pe_col[h, : len(cols)] = cols
             heads.append(dict(route=0, rowptr=rp, cols=cols))
-    for name, arr in (("route", route), ("vs_count", vs_count), ("vs_vertical", vs_vertical),
-                      ("vs_slash", vs_slash), ("pe_rowptr", pe_rowptr), ("pe_col", pe_col)):
-        getattr(bufs, name).copy_(torch.from_numpy(arr).to(getattr(bufs, name).device))
+    for field, arr in (("route", route), ("vs_count", vs_count), ("vs_vertical", vs_vertical),
+                       ("vs_slash", vs_slash), ("pe_rowptr", pe_rowptr), ("pe_col", pe_col)):
+        getattr(bufs, field).copy_(torch.from_numpy(arr).to(getattr(bufs, field).device))
     ref = dict(heads=heads)
     run_sparse(spec, X, bufs)
     bad = compare_tile_lists(spec, bufs, ref)
     assert not bad, "\n".join(bad[:20])
-    _check_attention(wl, I, X, spec, bufs, ref, synth.sample_rows(wl), "caller-supplied index sets")
+    rows = None if name == "tiny" else synth.sample_rows(wl)
+    _check_attention(wl, I, X, spec, bufs, ref, rows, f"caller-supplied index sets {name}")
 
 
 # Every middle block ties (Q = K = 0), and one head carries a 12-nat bias on the main
